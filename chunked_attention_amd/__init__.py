@@ -1,0 +1,290 @@
+"""Python binding of libkvc.so: chunk-causal sink+window attention over a
+bounded KV cache on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the path (cache writes, attention)
+runs in the library's HIP kernels; PyTorch supplies device memory and
+streams.  There is no fallback: if libkvc.so is missing or fails to load,
+importing the library raises.
+
+The C entry points keep their names here (``kvc_create``,
+``kvc_append_chunk``, ``chunk_attn_fwd``, ``kvc_evict``, ...), taking torch
+tensors where the C ABI takes device pointers.  :class:`Ring` wraps one ring
+with its device buffer.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkvc.so")
+
+KVC_OK = 0
+KVC_E_INVAL = -1
+KVC_E_STATE = -2
+KVC_E_NOMEM = -3
+KVC_E_DEVICE = -4
+KVC_E_UNSUPPORTED = -5
+
+KVC_KV_BF16 = 0
+KVC_KV_FP8_E4M3 = 1
+KVC_COND = 0
+KVC_STAGE = 1
+KVC_COMMIT = 2
+KVC_PHASE_EMPTY = 0
+KVC_PHASE_STAGED = 1
+KVC_PHASE_COMMITTED = 2
+KVC_MAX_WINDOW = 29
+KVC_TILE_KEYS = 64
+KVC_ALIGN = 256
+
+_DTYPES = {"bf16": KVC_KV_BF16, "fp8_e4m3": KVC_KV_FP8_E4M3}
+
+
+class kvc_config(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("chunk_tokens", ctypes.c_int32), ("cond_tokens", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class kvc_info(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "chunk", "phase", "cond_valid", "sink_valid", "n_window", "kv_len", "n_segments",
+        "free_slots")]
+
+
+class kvc_segment(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("chunk", "slot", "rows", "role")]
+
+
+class kvc_slot_view(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("vt", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("pitch", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+EXPORTS = (
+    "kvc_required_bytes", "kvc_create", "kvc_append_chunk", "chunk_attn_fwd", "kvc_evict",
+    "kvc_destroy", "kvc_status_str", "kvc_get_info", "kvc_get_segments", "kvc_get_slot",
+)
+
+
+def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Attach C signatures (kvc.h) to a loaded library."""
+    P = ctypes.c_void_p
+    I = ctypes.c_int32
+    lib.kvc_required_bytes.argtypes = [ctypes.POINTER(kvc_config)]
+    lib.kvc_required_bytes.restype = ctypes.c_size_t
+    lib.kvc_create.argtypes = [ctypes.POINTER(kvc_config), P, ctypes.c_size_t,
+                               ctypes.POINTER(P)]
+    lib.kvc_create.restype = I
+    lib.kvc_append_chunk.argtypes = [P, I, P, P, P]
+    lib.kvc_append_chunk.restype = I
+    lib.chunk_attn_fwd.argtypes = [P, P, P, P, P]
+    lib.chunk_attn_fwd.restype = I
+    lib.kvc_evict.argtypes = [P, ctypes.POINTER(I)]
+    lib.kvc_evict.restype = I
+    lib.kvc_destroy.argtypes = [P]
+    lib.kvc_destroy.restype = I
+    lib.kvc_status_str.argtypes = [I]
+    lib.kvc_status_str.restype = ctypes.c_char_p
+    lib.kvc_get_info.argtypes = [P, ctypes.POINTER(kvc_info)]
+    lib.kvc_get_info.restype = I
+    lib.kvc_get_segments.argtypes = [P, ctypes.POINTER(kvc_segment), I, ctypes.POINTER(I)]
+    lib.kvc_get_segments.restype = I
+    lib.kvc_get_slot.argtypes = [P, I, ctypes.POINTER(kvc_slot_view)]
+    lib.kvc_get_slot.restype = I
+    return lib
+
+
+_lib: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvc.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m chunked_attention_amd.build` "
+                "(there is no fallback path)")
+        _lib = declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)}")
+
+
+def status_str(status: int) -> str:
+    return lib().kvc_status_str(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != KVC_OK:
+        raise KvcError(status, what)
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_config(heads: int, head_dim: int, chunk_tokens: int, cond_tokens: int, window: int,
+                kv_dtype: str = "bf16", softmax_scale: float = 0.0) -> kvc_config:
+    return kvc_config(heads, head_dim, chunk_tokens, cond_tokens, window, _DTYPES[kv_dtype],
+                      softmax_scale)
+
+
+# ---- the C entry points, over torch tensors --------------------------------
+
+def kvc_required_bytes(cfg: kvc_config) -> int:
+    return lib().kvc_required_bytes(ctypes.byref(cfg))
+
+
+def kvc_create(cfg: kvc_config, dev_buf) -> ctypes.c_void_p:
+    handle = ctypes.c_void_p()
+    _check(lib().kvc_create(ctypes.byref(cfg), ctypes.c_void_p(dev_buf.data_ptr()),
+                            dev_buf.numel() * dev_buf.element_size(), ctypes.byref(handle)),
+           "kvc_create")
+    return handle
+
+
+def _check_tokens(x, rows: int, cfg: kvc_config, what: str) -> None:
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous bf16 CUDA tensor")
+    if tuple(x.shape) != (rows, cfg.heads, cfg.head_dim):
+        raise ValueError(f"{what} has shape {tuple(x.shape)}, expected "
+                         f"{(rows, cfg.heads, cfg.head_dim)}")
+
+
+def kvc_append_chunk(handle, cfg: kvc_config, kind: int, k, v, stream=None) -> None:
+    rows = cfg.cond_tokens if kind == KVC_COND else cfg.chunk_tokens
+    _check_tokens(k, rows, cfg, "k")
+    _check_tokens(v, rows, cfg, "v")
+    _check(lib().kvc_append_chunk(handle, kind, ctypes.c_void_p(k.data_ptr()),
+                                  ctypes.c_void_p(v.data_ptr()), _stream_handle(stream)),
+           "kvc_append_chunk")
+
+
+def chunk_attn_fwd(handle, cfg: kvc_config, q, o, lse=None, stream=None) -> None:
+    import torch
+    _check_tokens(q, cfg.chunk_tokens, cfg, "q")
+    _check_tokens(o, cfg.chunk_tokens, cfg, "o")
+    lse_ptr = None
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_contiguous() or \
+                tuple(lse.shape) != (cfg.heads, cfg.chunk_tokens):
+            raise ValueError("lse must be a contiguous float32 [heads, chunk_tokens] tensor")
+        lse_ptr = lse.data_ptr()
+    _check(lib().chunk_attn_fwd(handle, ctypes.c_void_p(q.data_ptr()),
+                                ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(lse_ptr),
+                                _stream_handle(stream)), "chunk_attn_fwd")
+
+
+def kvc_evict(handle) -> int:
+    ev = ctypes.c_int32(-1)
+    _check(lib().kvc_evict(handle, ctypes.byref(ev)), "kvc_evict")
+    return ev.value
+
+
+def kvc_destroy(handle) -> None:
+    lib().kvc_destroy(handle)
+
+
+def kvc_get_info(handle) -> kvc_info:
+    info = kvc_info()
+    _check(lib().kvc_get_info(handle, ctypes.byref(info)), "kvc_get_info")
+    return info
+
+
+def kvc_get_segments(handle) -> list[tuple[int, int, int, int]]:
+    buf = (kvc_segment * 32)()
+    count = ctypes.c_int32()
+    _check(lib().kvc_get_segments(handle, buf, 32, ctypes.byref(count)), "kvc_get_segments")
+    return [(s.chunk, s.slot, s.rows, s.role) for s in buf[:count.value]]
+
+
+def kvc_get_slot(handle, which: int) -> kvc_slot_view:
+    view = kvc_slot_view()
+    _check(lib().kvc_get_slot(handle, which, ctypes.byref(view)), "kvc_get_slot")
+    return view
+
+
+class Ring:
+    """One KV ring (one layer) in a torch-allocated device buffer."""
+
+    def __init__(self, heads: int, head_dim: int, chunk_tokens: int, cond_tokens: int,
+                 window: int, kv_dtype: str = "bf16", softmax_scale: float = 0.0,
+                 device="cuda"):
+        import torch
+        self.cfg = make_config(heads, head_dim, chunk_tokens, cond_tokens, window, kv_dtype,
+                               softmax_scale)
+        nbytes = kvc_required_bytes(self.cfg)
+        if nbytes == 0:
+            raise KvcError(KVC_E_INVAL, "kvc_required_bytes")
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.handle = kvc_create(self.cfg, self.buf)
+
+    def close(self) -> None:
+        if self.handle is not None:
+            kvc_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def cond(self, k, v, stream=None) -> None:
+        kvc_append_chunk(self.handle, self.cfg, KVC_COND, k, v, stream)
+
+    def stage(self, k, v, stream=None) -> None:
+        kvc_append_chunk(self.handle, self.cfg, KVC_STAGE, k, v, stream)
+
+    def commit(self, k, v, stream=None) -> None:
+        kvc_append_chunk(self.handle, self.cfg, KVC_COMMIT, k, v, stream)
+
+    def attention(self, q, out=None, lse=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty_like(q)
+        chunk_attn_fwd(self.handle, self.cfg, q, out, lse, stream)
+        return out
+
+    def evict(self) -> int:
+        return kvc_evict(self.handle)
+
+    def info(self) -> kvc_info:
+        return kvc_get_info(self.handle)
+
+    def segments(self):
+        return kvc_get_segments(self.handle)
+
+    def slot_tensors(self, which: int):
+        """Views of a stored slot: K [H][pitch][d], Vt [H][d][pitch] (bf16 or
+        uint8 codes) and, for fp8 rings, the float32 scales [H] of K and V."""
+        import torch
+        v = kvc_get_slot(self.handle, which)
+        base = self.buf.data_ptr()
+        H, d = self.cfg.heads, self.cfg.head_dim
+        n = H * v.pitch * d * v.elem_bytes
+
+        def part(ptr, nbytes):
+            return self.buf[ptr - base: ptr - base + nbytes]
+        dt = torch.bfloat16 if v.elem_bytes == 2 else torch.uint8
+        k = part(v.k, n).view(dt).view(H, v.pitch, d)
+        vt = part(v.vt, n).view(dt).view(H, d, v.pitch)
+        if v.k_scale:
+            ks = part(v.k_scale, 4 * H).view(torch.float32)
+            vs = part(v.v_scale, 4 * H).view(torch.float32)
+            return k, vt, ks, vs, v.rows
+        return k, vt, None, None, v.rows

@@ -1,0 +1,247 @@
+// K1: fused cache write.  Moves a chunk's K/V from the caller's token-major
+// layout [rows][H][d] into a ring slot: K head-major [H][pitch][d] and V
+// transposed per head [H][d][pitch] (the layout the attention kernel's PV
+// product reads), zero-filling the padded rows.  The fp8 variant quantises to
+// E4M3 with one float32 scale per (head, slot).
+//
+// The cached state is the clean K/V of each generated chunk, kept for the
+// chunks that follow (discuss.pytorch.kr "JoyAI-Video-Edit 소개", real-time
+// deployment section: after generation the clean KV is cached; the pages'
+// per-chunk table lists this save step as its own stage).
+//
+// HBM-bound: each element is read once and written once.  One workgroup
+// handles 64 rows of one head; V goes through LDS for the transpose.
+#include "device_common.hpp"
+#include "e4m3.hpp"
+#include "kvc_internal.hpp"
+
+namespace kvc {
+namespace {
+
+constexpr int kRowsPerBlock = kTileKeys;   // 64
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- bf16 ----
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void cache_write_bf16(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int rows, int pitch,
+    int heads, uint16_t* __restrict__ kd, uint16_t* __restrict__ vtd) {
+  constexpr int kChunks = D / 8;         // 16-byte chunks per row
+  constexpr int kLdsPitch = D + 2;       // u16 per LDS row; odd word count avoids conflicts
+  __shared__ uint32_t vtile32[kRowsPerBlock * kLdsPitch / 2];
+  uint16_t* vtile = reinterpret_cast<uint16_t*>(vtile32);
+
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  const int tid = threadIdx.x;
+
+  for (int c = tid; c < kRowsPerBlock * kChunks; c += kThreads) {
+    const int row = c / kChunks;
+    const int ch = c % kChunks;
+    const int r = r0 + row;
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (r < rows) {
+      const size_t src = (static_cast<size_t>(r) * heads + h) * D + ch * 8;
+      kv = ld16(k + src);
+      vv = ld16(v + src);
+    }
+    st16(kd + (static_cast<size_t>(h) * pitch + r) * D + ch * 8, kv);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vtile + row * kLdsPitch + ch * 8);
+    dst[0] = vv.x;
+    dst[1] = vv.y;
+    dst[2] = vv.z;
+    dst[3] = vv.w;
+  }
+  __syncthreads();
+  // transposed store: row dd of Vt gets 64 consecutive keys (8 chunks of 8)
+  for (int c = tid; c < D * 8; c += kThreads) {
+    const int dd = c / 8;
+    const int ch = c % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = vtile[(ch * 8 + 2 * j) * kLdsPitch + dd];
+      const uint32_t hi = vtile[(ch * 8 + 2 * j + 1) * kLdsPitch + dd];
+      w[j] = lo | (hi << 16);
+    }
+    st16(vtd + (static_cast<size_t>(h) * D + dd) * pitch + r0 + ch * 8,
+         make_uint4(w[0], w[1], w[2], w[3]));
+  }
+}
+
+// ----------------------------------------------------------------- fp8 ----
+// Pass 1: per (head, 64-row block) largest magnitude of K and of V.
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void cache_amax_fp8(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int rows, int heads,
+    float* __restrict__ partial /* [2][H][nblk] */) {
+  constexpr int kChunks = D / 8;
+  __shared__ float red[2][kThreads / 64];
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  const int nblk = gridDim.x;
+  const int tid = threadIdx.x;
+  float ak = 0.f, av = 0.f;
+  for (int c = tid; c < kRowsPerBlock * kChunks; c += kThreads) {
+    const int r = r0 + c / kChunks;
+    if (r >= rows) break;
+    const size_t src = (static_cast<size_t>(r) * heads + h) * D + (c % kChunks) * 8;
+    const uint4 kv = ld16(k + src);
+    const uint4 vv = ld16(v + src);
+    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+    const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ak = fmaxf(ak, fabsf(bf16_bits_to_float(kw[j] & 0xFFFFu)));
+      ak = fmaxf(ak, fabsf(bf16_bits_to_float(kw[j] >> 16)));
+      av = fmaxf(av, fabsf(bf16_bits_to_float(vw[j] & 0xFFFFu)));
+      av = fmaxf(av, fabsf(bf16_bits_to_float(vw[j] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    ak = fmaxf(ak, __shfl_xor(ak, off));
+    av = fmaxf(av, __shfl_xor(av, off));
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = ak;
+    red[1][tid >> 6] = av;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float mk = 0.f, mv = 0.f;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      mk = fmaxf(mk, red[0][w]);
+      mv = fmaxf(mv, red[1][w]);
+    }
+    partial[(0 * heads + h) * nblk + blockIdx.x] = mk;
+    partial[(1 * heads + h) * nblk + blockIdx.x] = mv;
+  }
+}
+
+// Pass 2: reduce the partials of the head, derive s = amax / 448 (float32,
+// correctly rounded; 1 when amax = 0), write E4M3 codes of x / s.
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void cache_quant_fp8(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int rows, int pitch,
+    int heads, int nblk_rows, const float* __restrict__ partial, uint8_t* __restrict__ kd,
+    uint8_t* __restrict__ vtd, float* __restrict__ k_scale, float* __restrict__ v_scale) {
+  constexpr int kChunks = D / 8;         // 8-element chunks per row
+  constexpr int kLdsPitch = D + 4;       // bytes per LDS row of codes
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[kRowsPerBlock * kLdsPitch];
+  __shared__ float sc[2];
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  const int tid = threadIdx.x;
+
+  if (tid < 64) {
+    float mk = 0.f, mv = 0.f;
+    for (int b = tid; b < nblk_rows; b += 64) {
+      mk = fmaxf(mk, partial[(0 * heads + h) * nblk_rows + b]);
+      mv = fmaxf(mv, partial[(1 * heads + h) * nblk_rows + b]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mk = fmaxf(mk, __shfl_xor(mk, off));
+      mv = fmaxf(mv, __shfl_xor(mv, off));
+    }
+    if (tid == 0) {
+      const float sk = mk > 0.f ? __fdiv_rn(mk, 448.0f) : 1.0f;
+      const float sv = mv > 0.f ? __fdiv_rn(mv, 448.0f) : 1.0f;
+      sc[0] = sk;
+      sc[1] = sv;
+      if (blockIdx.x == 0) {
+        k_scale[h] = sk;
+        v_scale[h] = sv;
+      }
+    }
+  }
+  __syncthreads();
+  const float sk = sc[0], sv = sc[1];
+
+  for (int c = tid; c < kRowsPerBlock * kChunks; c += kThreads) {
+    const int row = c / kChunks;
+    const int ch = c % kChunks;
+    const int r = r0 + row;
+    uint32_t kc[2] = {0u, 0u}, vc[2] = {0u, 0u};
+    if (r < rows) {
+      const size_t src = (static_cast<size_t>(r) * heads + h) * D + ch * 8;
+      const uint4 kv = ld16(k + src);
+      const uint4 vv = ld16(v + src);
+      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t k0 = e4m3_from_float(__fdiv_rn(bf16_bits_to_float(kw[j] & 0xFFFFu), sk));
+        const uint32_t k1 = e4m3_from_float(__fdiv_rn(bf16_bits_to_float(kw[j] >> 16), sk));
+        const uint32_t v0 = e4m3_from_float(__fdiv_rn(bf16_bits_to_float(vw[j] & 0xFFFFu), sv));
+        const uint32_t v1 = e4m3_from_float(__fdiv_rn(bf16_bits_to_float(vw[j] >> 16), sv));
+        kc[j >> 1] |= (k0 | (k1 << 8)) << (16 * (j & 1));
+        vc[j >> 1] |= (v0 | (v1 << 8)) << (16 * (j & 1));
+      }
+    }
+    *reinterpret_cast<uint2*>(kd + (static_cast<size_t>(h) * pitch + r) * D + ch * 8) =
+        make_uint2(kc[0], kc[1]);
+    // LDS rows are 4-byte aligned only: two 32-bit stores
+    uint32_t* vdst = reinterpret_cast<uint32_t*>(vtile + row * kLdsPitch + ch * 8);
+    vdst[0] = vc[0];
+    vdst[1] = vc[1];
+  }
+  __syncthreads();
+  // transposed store: row dd of Vt gets 64 consecutive keys (4 chunks of 16)
+  for (int c = tid; c < D * 4; c += kThreads) {
+    const int dd = c / 4;
+    const int ch = c % 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        x |= static_cast<uint32_t>(vtile[(ch * 16 + 4 * j + b) * kLdsPitch + dd]) << (8 * b);
+      w[j] = x;
+    }
+    st16(vtd + (static_cast<size_t>(h) * D + dd) * pitch + r0 + ch * 16,
+         make_uint4(w[0], w[1], w[2], w[3]));
+  }
+}
+
+template <int D>
+kvc_status launch_write(const CacheWriteDesc& d, hipStream_t s) {
+  const dim3 block(kThreads);
+  const dim3 grid(d.pitch / kRowsPerBlock, d.heads);
+  if (d.kv_dtype == KVC_KV_BF16) {
+    hipLaunchKernelGGL(cache_write_bf16<D>, grid, block, 0, s,
+                       static_cast<const uint16_t*>(d.k), static_cast<const uint16_t*>(d.v),
+                       d.rows, d.pitch, d.heads, static_cast<uint16_t*>(d.k_dst),
+                       static_cast<uint16_t*>(d.vt_dst));
+  } else {
+    const int nblk = (d.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(cache_amax_fp8<D>, dim3(nblk, d.heads), block, 0, s,
+                       static_cast<const uint16_t*>(d.k), static_cast<const uint16_t*>(d.v),
+                       d.rows, d.heads, d.scratch);
+    hipLaunchKernelGGL(cache_quant_fp8<D>, grid, block, 0, s,
+                       static_cast<const uint16_t*>(d.k), static_cast<const uint16_t*>(d.v),
+                       d.rows, d.pitch, d.heads, nblk, d.scratch,
+                       static_cast<uint8_t*>(d.k_dst), static_cast<uint8_t*>(d.vt_dst),
+                       d.k_scale, d.v_scale);
+  }
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_DEVICE;
+}
+
+}  // namespace
+
+kvc_status launch_cache_write(const CacheWriteDesc& d, void* stream) {
+  if (d.rows <= 0 || d.pitch % kRowsPerBlock || d.pitch < d.rows) return KVC_E_INVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d.head_dim) {
+    case 64: return launch_write<64>(d, s);
+    case 128: return launch_write<128>(d, s);
+    default: return KVC_E_UNSUPPORTED;
+  }
+}
+
+}  // namespace kvc

@@ -1,0 +1,79 @@
+// Internal interface between the host ring logic (ring.cpp, plain C++) and
+// the device launchers (launch_*.hip).  Nothing here includes HIP headers, so
+// the ring logic builds and is tested on a host without a GPU against a
+// recording launcher.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+constexpr int kMaxSegments = KVC_MAX_WINDOW + 3;   // cond + sink + W + current
+constexpr int kTileKeys = KVC_TILE_KEYS;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int pad_rows(int r) { return (r + kTileKeys - 1) / kTileKeys * kTileKeys; }
+
+// One stored slot of R rows (see kvc.h for the layout).
+struct SlotGeom {
+  int rows = 0;        // R
+  int pitch = 0;       // P, R rounded up to kTileKeys
+  size_t k_off = 0;    // byte offsets from the ring base
+  size_t vt_off = 0;
+  size_t scale_off = 0;  // float32 [2][H]; only for fp8 rings
+  size_t bytes = 0;      // total bytes of the slot
+};
+
+// Description of one cache write (condition rows or a chunk).
+struct CacheWriteDesc {
+  const void* k = nullptr;     // [rows][H][d] bf16, token-major
+  const void* v = nullptr;
+  int rows = 0;
+  int pitch = 0;
+  int heads = 0;
+  int head_dim = 0;
+  int kv_dtype = KVC_KV_BF16;
+  void* k_dst = nullptr;       // [H][pitch][d]
+  void* vt_dst = nullptr;      // [H][d][pitch]
+  float* k_scale = nullptr;    // [H] (fp8)
+  float* v_scale = nullptr;    // [H] (fp8)
+  float* scratch = nullptr;    // fp8: float32 [2][H][pitch/kTileKeys] partial amax
+};
+
+// One logical segment of the visible KV, in device terms.
+struct AttnSegment {
+  const void* k = nullptr;      // [H][pitch][d]
+  const void* vt = nullptr;     // [H][d][pitch]
+  const float* k_scale = nullptr;
+  const float* v_scale = nullptr;
+  int rows = 0;
+  int pitch = 0;
+};
+
+struct AttnDesc {
+  const void* q = nullptr;      // [n][H][d] bf16
+  void* o = nullptr;            // [n][H][d] bf16
+  float* lse = nullptr;         // [H][n] or null
+  int n = 0;
+  int heads = 0;
+  int head_dim = 0;
+  int kv_dtype = KVC_KV_BF16;
+  float scale = 0.f;            // softmax scale (natural-log units)
+  int nseg = 0;
+  AttnSegment seg[kMaxSegments];
+  void* workspace = nullptr;    // device scratch for split partials
+  size_t workspace_bytes = 0;
+};
+
+// Launchers.  Return KVC_OK or KVC_E_DEVICE / KVC_E_UNSUPPORTED.  The device
+// implementation lives in the HIP sources; tests link a recording fake.
+kvc_status launch_cache_write(const CacheWriteDesc& d, void* stream);
+kvc_status launch_attention(const AttnDesc& d, void* stream);
+
+// Workspace bytes the attention launcher may use for a ring of this shape.
+size_t attention_workspace_bytes(int heads, int head_dim, int n, int kv_dtype);
+
+}  // namespace kvc

@@ -1,0 +1,222 @@
+/*
+ * kvc.h -- chunk-causal sink+window attention over a bounded KV cache, gfx950.
+ *
+ * The method (JoyAI-Video-Edit): a video stream is cut into chunks (one latent
+ * frame = 8 video frames each).  The queries of the chunk being generated
+ * attend
+ *   - every key of their own chunk (bidirectional inside the chunk),
+ *   - the condition tokens (always visible),
+ *   - the first chunk of the stream, kept as a global sink, and
+ *   - a sliding window of the W most recent earlier chunks,
+ * so the attended set, and with it per-chunk cost and memory, stays bounded
+ * however long the stream runs.  After a chunk is generated its clean K/V is
+ * cached for later chunks; the cache keeps only the sink and the window.
+ * Sources: discuss.pytorch.kr "JoyAI-Video-Edit 소개", sections on the
+ * chunk-wise autoregressive adaptation (paper section 4.1) and the real-time
+ * deployment pipeline (paper section 5); ta-paperlens "論文解説:
+ * JoyAI-Video-Edit", sections 4.1 and 5 (per-chunk loop: denoise with the
+ * cache as history, then update the cache keeping window + sink).
+ *
+ * Conventions for every call:
+ *   - Status codes are the KVC_* values below; 0 is success, errors are
+ *     negative.  After any error the ring's state is unchanged.
+ *   - Device pointers are plain HIP device addresses owned by the caller;
+ *     the library never allocates device memory and never frees what it is
+ *     given.  Streams are hipStream_t passed as void* (NULL = null stream).
+ *   - Work is enqueued asynchronously on the given stream; no call
+ *     synchronises the host with the device.  Calls on one ring must be made
+ *     from one host thread in program order, and their device work must be
+ *     ordered (same stream, or ordered by the caller).  Distinct rings are
+ *     independent.
+ *   - Tensors are row-major, token-major bf16 unless stated:
+ *     [rows][heads][head_dim], contiguous, 16-byte aligned base.
+ *   - Inputs holding NaN or Inf are not checked; they propagate.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvc_status;
+#define KVC_OK             0
+#define KVC_E_INVAL       (-1)  /* bad argument: config, null or misaligned pointer */
+#define KVC_E_STATE       (-2)  /* call not allowed in the ring's current state */
+#define KVC_E_NOMEM       (-3)  /* caller buffer smaller than kvc_required_bytes */
+#define KVC_E_DEVICE      (-4)  /* the HIP runtime reported an error */
+#define KVC_E_UNSUPPORTED (-5)  /* valid request this build does not implement */
+
+/* K/V storage type of a ring */
+#define KVC_KV_BF16      0   /* bf16, bit copies of the caller's K/V */
+#define KVC_KV_FP8_E4M3  1   /* OCP E4M3 codes + one float32 scale per (head, stored chunk) */
+
+/* kinds for kvc_append_chunk */
+#define KVC_COND    0   /* condition tokens (m rows) */
+#define KVC_STAGE   1   /* K/V of the current chunk for the present denoise step */
+#define KVC_COMMIT  2   /* clean K/V of the current chunk, kept as history */
+
+/* ring phases reported by kvc_get_info */
+#define KVC_PHASE_EMPTY      0   /* no current chunk */
+#define KVC_PHASE_STAGED     1   /* current chunk holds staged (noisy) K/V */
+#define KVC_PHASE_COMMITTED  2   /* current chunk was committed, not yet evicted */
+
+#define KVC_MAX_WINDOW   29       /* W <= 29: at most 32 visible segments */
+#define KVC_TILE_KEYS    64       /* stored rows are padded to a multiple of this */
+#define KVC_ALIGN        256      /* dev_buf alignment */
+
+typedef struct kvc_config {
+  int32_t heads;          /* H >= 1 */
+  int32_t head_dim;       /* d, 64 or 128 */
+  int32_t chunk_tokens;   /* n >= 1: query and key tokens per chunk */
+  int32_t cond_tokens;    /* m >= 0: condition tokens (keys/values only) */
+  int32_t window;         /* W, 0..KVC_MAX_WINDOW: earlier chunks kept besides the sink */
+  int32_t kv_dtype;       /* KVC_KV_BF16 or KVC_KV_FP8_E4M3 */
+  float softmax_scale;    /* > 0, or 0 for 1/sqrt(head_dim) */
+} kvc_config;
+
+typedef struct kvc_ring kvc_ring;   /* opaque host handle */
+
+/*
+ * Bytes of device memory a ring with this config needs (cache slots,
+ * per-slot scales, scratch), or 0 if the config is invalid.
+ *
+ * Layout of dev_buf (for tests and tools; callers only need the size): one
+ * slot for the m condition rows (none if m = 0) followed by W + 2 slots of n
+ * rows (sink, W window chunks, one staging slot).  A slot of R rows stores,
+ * with P = R rounded up to KVC_TILE_KEYS and e = 2 (bf16) or 1 (fp8) bytes:
+ *   K  [H][P][d]  (key-major)        -- rows >= R are zero
+ *   Vt [H][d][P]  (value, transposed) -- columns >= R are zero
+ *   scales float32 [2][H] (K then V; fp8 rings only)
+ * each part starting on a KVC_ALIGN boundary.
+ */
+size_t kvc_required_bytes(const kvc_config* cfg);
+
+/*
+ * Create a ring in caller-owned device memory.
+ *   cfg      config as above (copied).
+ *   dev_buf  device memory of at least kvc_required_bytes(cfg) bytes, aligned
+ *            to KVC_ALIGN.  Owned by the caller; must outlive the ring.  Its
+ *            contents need no initialisation.
+ *   out      receives the handle.
+ * Host-only: no device work, no allocation of device memory.
+ * Errors: KVC_E_INVAL (bad config, null pointer, misaligned dev_buf),
+ *         KVC_E_NOMEM (bytes < required).
+ */
+kvc_status kvc_create(const kvc_config* cfg, void* dev_buf, size_t bytes, kvc_ring** out);
+
+/*
+ * Write K/V rows into the cache (the fused cache-write kernel).
+ *   kind = KVC_COND:   k, v are [m][H][d]; (re)writes the condition slot.
+ *                      Allowed in any phase; m must be > 0.
+ *   kind = KVC_STAGE:  k, v are [n][H][d], the current chunk's K/V for this
+ *                      denoise step.  From phase EMPTY it takes a free slot
+ *                      as staging slot (KVC_E_STATE if none: the previous
+ *                      chunk was not evicted); from STAGED it overwrites the
+ *                      staging slot (next denoise step).  Not allowed when
+ *                      COMMITTED (call kvc_evict first).
+ *   kind = KVC_COMMIT: k, v are [n][H][d], the clean K/V of the current chunk
+ *                      after its denoise steps.  Written into the staging slot
+ *                      (or a free slot from phase EMPTY) and published: as the
+ *                      sink if this is chunk 0, else as the newest window
+ *                      chunk.  Not allowed when already COMMITTED.
+ * bf16 rings store bit copies; fp8 rings store E4M3 codes of x/s with
+ * s = amax/448 per (head, slot), amax over that head's rows and features,
+ * s = 1 when amax = 0 (nearest, ties to even, saturating).
+ * The caller's k, v must stay valid until the stream reaches this work.
+ * Errors: KVC_E_INVAL (null/misaligned pointers, unknown kind, COND with
+ * m = 0), KVC_E_STATE, KVC_E_DEVICE.
+ */
+kvc_status kvc_append_chunk(kvc_ring* ring, int32_t kind, const void* k, const void* v,
+                            void* stream);
+
+/*
+ * Chunk-causal attention of the current chunk's queries.
+ *   q    [n][H][d] bf16 queries of the current chunk.
+ *   o    [n][H][d] bf16 output, o_i = sum_j softmax_j(scale <q_i, k_j>) v_j
+ *        over the visible keys, in logical order [condition ; sink (chunk 0,
+ *        for chunks >= 1) ; window chunks max(1, t-W) .. t-1 ; current chunk
+ *        t].  Sink and window use committed clean K/V; the current chunk uses
+ *        the staged K/V (phase STAGED) or its committed K/V (COMMITTED).
+ *   lse  optional [H][n] float32 natural-log log-sum-exp of the scaled
+ *        logits per query (NULL to skip).
+ * q may not alias o.  No concatenated KV is formed: the kernel walks the
+ * cache slots in logical order.
+ * Errors: KVC_E_INVAL (null/misaligned pointers), KVC_E_STATE (phase EMPTY,
+ * or condition tokens configured but never written), KVC_E_DEVICE.
+ */
+kvc_status chunk_attn_fwd(kvc_ring* ring, const void* q, void* o, float* lse, void* stream);
+
+/*
+ * Finish the current committed chunk and recycle cache memory (host only).
+ * If more than W window chunks are held, the oldest is dropped and its slot
+ * becomes free for the next chunk's staging; the sink is never dropped.
+ *   evicted  optional; receives the dropped chunk id, or -1 if none.
+ * From phase COMMITTED the ring moves to EMPTY for the next chunk id.  From
+ * EMPTY it is a no-op (-1).  From STAGED: KVC_E_STATE.
+ */
+kvc_status kvc_evict(kvc_ring* ring, int32_t* evicted);
+
+/* Free the host handle (not dev_buf).  NULL is accepted. */
+kvc_status kvc_destroy(kvc_ring* ring);
+
+/* Static string naming a status code. */
+const char* kvc_status_str(kvc_status status);
+
+/* ---- introspection (host only) ---- */
+
+typedef struct kvc_info {
+  int32_t chunk;        /* current chunk id (the next one in phase EMPTY) */
+  int32_t phase;        /* KVC_PHASE_* */
+  int32_t cond_valid;   /* condition slot written */
+  int32_t sink_valid;   /* chunk 0 committed */
+  int32_t n_window;     /* committed window chunks held (sink excluded) */
+  int32_t kv_len;       /* keys an attention call would attend now, 0 if none */
+  int32_t n_segments;   /* segments of that call */
+  int32_t free_slots;   /* chunk slots holding nothing */
+} kvc_info;
+
+kvc_status kvc_get_info(const kvc_ring* ring, kvc_info* out);
+
+typedef struct kvc_segment {
+  int32_t chunk;        /* chunk id, or -1 for the condition tokens */
+  int32_t slot;         /* chunk slot index 0..W+1, or -1 for the condition slot */
+  int32_t rows;         /* valid rows */
+  int32_t role;         /* 0 cond, 1 sink, 2 window, 3 current */
+} kvc_segment;
+
+/*
+ * The logical segment table an attention call would walk now, in order.
+ * Writes at most cap entries to out and the full count to *count.
+ * KVC_E_STATE if no attention call is possible now.
+ */
+kvc_status kvc_get_segments(const kvc_ring* ring, kvc_segment* out, int32_t cap,
+                            int32_t* count);
+
+typedef struct kvc_slot_view {
+  void* k;              /* K  [H][pitch][d] */
+  void* vt;             /* Vt [H][d][pitch] */
+  float* k_scale;       /* [H] (fp8 rings; NULL for bf16) */
+  float* v_scale;       /* [H] */
+  int32_t rows;         /* valid rows */
+  int32_t pitch;        /* padded rows */
+  int32_t elem_bytes;   /* 2 (bf16) or 1 (fp8) */
+  int32_t reserved;
+} kvc_slot_view;
+
+/*
+ * Device addresses of one stored slot, for reading the cache back:
+ * which = -1: condition slot; which = -2: the current chunk's slot (staged
+ * or committed); which >= 0: the slot holding that committed chunk id.
+ * KVC_E_STATE if that slot holds nothing.
+ */
+kvc_status kvc_get_slot(const kvc_ring* ring, int32_t which, kvc_slot_view* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif  /* KVC_H_ */

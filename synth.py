@@ -120,6 +120,7 @@ class Stream:
         self.dist = dist
         self.seed = w.seed if seed is None else seed
         self.pool = pool
+        self._cache: dict = {}
 
     def _key(self, layer: int, chunk: int, step: int) -> tuple[int, int, int]:
         if self.pool:
@@ -129,8 +130,14 @@ class Stream:
     def _t(self, layer, chunk, step, role, rows):
         w = self.w
         l, c, s = self._key(layer, chunk, step)
-        return draw(self.seed, l, c, s, role, (rows, w.heads, w.head_dim),
-                    _role_std(w, self.dist, role))
+        key = (l, c, s, role)
+        if self.pool and key in self._cache:
+            return self._cache[key]
+        x = draw(self.seed, l, c, s, role, (rows, w.heads, w.head_dim),
+                 _role_std(w, self.dist, role))
+        if self.pool:
+            self._cache[key] = x
+        return x
 
     def q(self, chunk: int, step: int = 0, layer: int = 0) -> torch.Tensor:
         return self._t(layer, chunk, step, "q", self.w.chunk_tokens)

@@ -1,0 +1,158 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded inputs.  Tolerances: bf16 max-abs <= 2e-2 and rel-L2 <= 5e-3
+over the whole output of a call."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_attention_amd as kv
+import synth
+from helpers import (StreamRun, assert_bf16_parity, compare, to_f64)
+from oracle import attention as O1
+
+pytestmark = pytest.mark.gpu
+
+
+def ring_for(w, **kw):
+    return kv.Ring(w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window,
+                   kv_dtype=kw.get("kv_dtype", w.kv_dtype))
+
+
+# ---------------------------------------------------------------- K1 ----
+
+@pytest.mark.parametrize("H,d,n,m", [(3, 128, 100, 40), (2, 64, 64, 16), (40, 128, 1620, 256),
+                                     (1, 128, 1, 1)])
+def test_cache_write_bf16_is_bit_exact(H, d, n, m):
+    w = synth.Workload("k1", H, d, n, m, 1, 3, seed=5)
+    s = synth.Stream(w, "sharp")
+    r = ring_for(w)
+    ck, cv = s.kv_cond()
+    r.cond(ck.cuda(), cv.cuda())
+    k, v = s.kv_noisy(0)
+    r.stage(k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    for which, (kk, vv) in ((-1, (ck, cv)), (-2, (k, v))):
+        K, Vt, _, _, rows = r.slot_tensors(which)
+        K, Vt = K.cpu(), Vt.cpu()
+        assert rows == kk.shape[0]
+        P = K.shape[1]
+        assert P % 64 == 0 and P >= rows
+        assert torch.equal(K[:, :rows].view(torch.int16), kk.permute(1, 0, 2).view(torch.int16))
+        assert torch.equal(Vt[:, :, :rows].view(torch.int16),
+                           vv.permute(1, 2, 0).contiguous().view(torch.int16))
+        assert (K[:, rows:].view(torch.int16) == 0).all()
+        assert (Vt[:, :, rows:].view(torch.int16) == 0).all()
+
+
+# ---------------------------------------------------------------- K2 ----
+
+@pytest.mark.parametrize("dist", ["baseline", "sharp", "peaky"])
+def test_tiny_stream_parity(dist):
+    w = synth.WORKLOADS["tiny"]
+    s = synth.Stream(w, dist)
+    run = StreamRun(s, ring_for(w))
+    for t in range(w.chunks):
+        (o, ref, st), = run.chunk(t, lse=True)
+        assert_bf16_parity(st, f"tiny {dist} t={t}")
+        assert st["lse_max_abs"] < 1e-3, st
+
+
+@pytest.mark.parametrize("shape", [
+    dict(heads=2, head_dim=128, chunk_tokens=1, cond_tokens=0, window=0),      # one query
+    dict(heads=3, head_dim=128, chunk_tokens=63, cond_tokens=5, window=1),     # ragged
+    dict(heads=1, head_dim=128, chunk_tokens=129, cond_tokens=64, window=2),   # 2 q tiles
+    dict(heads=4, head_dim=64, chunk_tokens=200, cond_tokens=1, window=3),
+    dict(heads=2, head_dim=128, chunk_tokens=300, cond_tokens=0, window=4),
+    dict(heads=5, head_dim=128, chunk_tokens=64, cond_tokens=128, window=0),   # exact tiles
+])
+@pytest.mark.parametrize("dist", ["sharp", "peaky"])
+def test_edge_shapes_parity(shape, dist):
+    w = synth.Workload("edge", chunks=shape["window"] + 4, seed=11, **shape)
+    run = StreamRun(synth.Stream(w, dist), ring_for(w))
+    for t in range(w.chunks):
+        (o, ref, st), = run.chunk(t, lse=True)
+        assert_bf16_parity(st, f"{shape} {dist} t={t}")
+        assert st["lse_max_abs"] < 2e-3, st
+
+
+@pytest.mark.parametrize("dist", ["baseline", "sharp", "peaky"])
+def test_720p_stream_parity_sampled_heads(dist):
+    # config: 40 heads x 128, 1620 queries, 256 condition tokens, W = 3;
+    # chunks 0..5 reach the full window (8356 keys from chunk 4).  The oracle
+    # runs on 3 heads; the GPU computes all 40.
+    w = synth.WORKLOADS["720p"]
+    heads = [0, 17, 39]
+    run = StreamRun(synth.Stream(w, dist), ring_for(w), heads=heads)
+    for t in range(6):
+        (o, ref, st), = run.chunk(t, lse=True)
+        assert_bf16_parity(st, f"720p {dist} t={t}")
+        assert st["lse_max_abs"] < 2e-3, st
+    assert run.ring.info().n_window == 3
+
+
+def test_720p_steady_chunk_all_heads():
+    # one steady-state chunk (t = 4, 8356 keys) checked on every head
+    w = synth.WORKLOADS["720p"]
+    run = StreamRun(synth.Stream(w, "baseline"), ring_for(w))
+    for t in range(4):
+        run.chunk(t, check=False)
+    (o, ref, st), = run.chunk(4)
+    assert_bf16_parity(st, "720p t=4 all heads")
+    assert O1.kv_length(4, 256, 1620, 3) == 8356
+
+
+@pytest.mark.parametrize("where", ["cond", "current"])
+@pytest.mark.parametrize("shift", [30.0, -30.0])
+def test_segment_offset_stress(where, shift):
+    # every logit against one segment moves by `shift`: exercises the running
+    # max and rescale path when the largest logits come first or last.
+    w = synth.Workload("stress", 4, 128, 200, 70, 2, 4, seed=21)
+    s = synth.Stream(w, "sharp")
+    r = ring_for(w)
+    ck, cv = s.kv_cond()
+    oracle_hist = []
+    q_all = {}
+    ckr = synth.zero_feature0(ck)
+    if where == "cond":
+        qd = s.q(0)
+        _, ckr = synth.offset_segment(qd, ck, shift, w.scale)
+    r.cond(ckr.cuda(), cv.cuda())
+    so = O1.StreamOracle(w.window, w.scale, O1.as_f64(ckr), O1.as_f64(cv))
+    for t in range(w.chunks):
+        k, v = s.kv_noisy(t)
+        q = s.q(t)
+        q = q.clone()
+        q[..., 0] = 1.0
+        if where == "current":
+            _, k = synth.offset_segment(q, k, shift, w.scale)
+        else:
+            k = synth.zero_feature0(k)
+        r.stage(k.cuda(), v.cuda())
+        o = r.attention(q.cuda())
+        ref, _ = so.attend(t, O1.as_f64(q), O1.as_f64(k), O1.as_f64(v))
+        st = compare(o, ref)
+        assert_bf16_parity(st, f"stress {where} {shift} t={t}")
+        kc, vc = s.kv_clean(t)
+        kc = synth.zero_feature0(kc)
+        r.commit(kc.cuda(), vc.cuda())
+        so.commit(t, O1.as_f64(kc), O1.as_f64(vc))
+        r.evict()
+
+
+def test_long_stream_sampled_chunks():
+    # W = 6 stream, 225 chunks from a pool of 4 input sets; parity on sampled
+    # chunks (3 heads), including the first window-full chunk and the last.
+    w = synth.WORKLOADS["long"]
+    heads = [0, 17, 39]
+    run = StreamRun(synth.Stream(w, "sharp", pool=4), ring_for(w), heads=heads)
+    check = {0, 6, 7, 100, 224}
+    for t in range(w.chunks):
+        out = run.chunk(t, check=t in check)
+        if t in check:
+            (o, ref, st), = out
+            assert_bf16_parity(st, f"long t={t}")
+    info = run.ring.info()
+    assert info.chunk == 225 and info.n_window == 6
