@@ -6,278 +6,637 @@
 // autoregressive adaptation section: bidirectional within the chunk, causal
 // across chunks through a sliding window plus the first chunk as global
 // sink).  The visible set is never concatenated: the kernel walks the ring's
-// segment table (slots in logical order) tile by tile.
+// segment table (cache slots in logical order) tile by tile.
 //
-// Work decomposition: one workgroup = 4 waves = 128 queries of one head; each
-// wave owns 32 queries for the whole key range.  Keys stream through LDS in
-// tiles of 64, double-buffered (the next tile's global loads are in flight
-// while the current one is computed).
+// Work: a "row" is 128 queries of one head (2 waves x 64 queries); its keys
+// are T tiles of 64 keys over all segments (a segment's last tile is masked).
+// The grid is persistent: nwg workgroups (two per CU) split the R*T
+// (row, tile) steps into equal contiguous ranges (stream-K), so the whole GPU
+// stays busy whatever R is.  A row cut between workgroups is finished by the
+// last piece to arrive, which merges the others' partial (O, max, sum) by
+// log-sum-exp.
 //
-// Per tile and wave, with 32x32x16 bf16 MFMAs (fp32 accumulate):
-//   S^T[64 keys x 32 q] = K_tile[64 x d] . Q^T[d x 32]     (A = K from LDS, B = Q in VGPRs)
-//   online softmax on S^T: each lane holds one query column, 32 key values
-//   O^T[d x 32 q]      += Vt_tile[d x 64] . P^T[64 x 32]    (A = Vt from LDS, B = P in VGPRs)
-// Computing the transposed scores puts P^T straight into the B-operand
-// layout of the PV product (no shuffle through LDS).  The 32x32 accumulator
-// holds rows (i/4)*8 + (lane/32)*4 + i%4 in register i; reading K rows through
-// the permutation pi (swap of row bits 2 and 3) makes the 8 keys each lane
-// contributes to one PV step consecutive, so the Vt operand is one 16-byte
-// LDS read.  Both LDS tiles are XOR-swizzled per row so the 16-byte reads of
-// 16 consecutive lanes hit distinct bank groups.
+// Per tile and wave (64 queries = 2 column blocks of 32), with 32x32x16 bf16
+// MFMAs (fp32 accumulate):
+//   S^T[64 keys x 64 q] = K_tile . Q^T      A = K from LDS, B = Q in VGPRs
+//   O^T[d x 64 q]      += Vt_tile . P^T     A = Vt from LDS, B = P in VGPRs
+// Computing transposed scores puts P^T straight into the B-operand layout of
+// the PV product.  The accumulator holds key rows (i/4)*8 + (lane/32)*4 + i%4
+// in register i; the ring stores V's key columns in exactly that order within
+// each group of 16 (kappa, a swap of index bits 2 and 3), so the 8 keys a
+// lane feeds to one PV step are consecutive and each Vt operand is one
+// 16-byte LDS read.  Tiles are XOR-swizzled per row (16-byte chunk c of row r
+// lives at c ^ (r & 7)) so 8 consecutive lanes' 16-byte reads hit distinct
+// bank groups; the swizzle depends only on the lane, so the unrolled reads of
+// one lane differ by immediate offsets.  K and Vt tiles are copied from
+// global memory straight into LDS (global_load_lds_dwordx4), two buffers
+// each.
 //
-// Online softmax in base 2: t = s * scale * log2(e); the running max is only
-// raised (and O, l rescaled) when a tile's max exceeds it by more than 8,
-// which keeps p = 2^(t - m) <= 2^8 and skips nearly every rescale after the
-// first tiles.  The row sum l is kept per lane and combined across the two
-// lane halves at the end.
+// Software pipeline: while the softmax of tile j runs on the VALU, the
+// QK^T MFMAs of tile j+1 are issued; then the PV MFMAs of tile j.  So K runs
+// one tile ahead of V: iteration j reads K_{j+1} and V_j while K_{j+2} and
+// V_{j+1} stream in.
+//
+// Softmax in base 2 with a fixed reference per row piece: t = s*scale*log2(e)
+// and p = 2^(t - m_ref), where m_ref is the max of the piece's first 32 keys.
+// Later keys may exceed m_ref; while they do so by less than 2^96 every p,
+// every partial sum and the accumulators stay finite in fp32 (and in bf16 for
+// P), so O never needs rescaling inside the loop.  The loop tracks the
+// largest logit it meets; if one ever exceeds m_ref by more than that margin,
+// the piece is computed again with m_ref set to that largest logit.  The row
+// sum is kept per lane and combined across the two lane halves at the end.
+#include <algorithm>
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kvc_internal.hpp"
 
 namespace kvc {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBq = 128;          // queries per workgroup
-constexpr int kBk = kTileKeys;    // keys per tile (64)
-constexpr float kRescaleThreshold = 8.0f;
+constexpr int kWaves = kAttnWaves;      // 2
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQW = 64;                 // queries per wave
+constexpr int kBq = kAttnRowQueries;    // queries per row (128)
+static_assert(kBq == kWaves * kQW, "row = waves x 64 queries");
+constexpr int kBk = kTileKeys;          // keys per tile (64)
+constexpr int kMaxWg = kAttnMaxWg;      // persistent workgroups at most (2 per CU)
+constexpr int kMinPieceTiles = 16;      // smallest share of a row worth splitting off
+constexpr float kRefMargin = 96.0f;       // log2 units above m_ref kept finite
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kMlPerWave = 2 * 3 * 32;  // partial (max, sum, exact sum) per query, 64 queries
 
 struct SegArg {
   const unsigned char* k;   // [H][pitch][d]
   const unsigned char* vt;  // [H][d][pitch]
   int rows;
   int pitch;
+  int tile0;                // first tile of this segment in the row's tile list
+  int pad_;
 };
 
 struct AttnArgs {
   const uint16_t* q;
   uint16_t* o;
   float* lse;
+  float* part_o;            // [2*nwg][kBq*D] partial O, accumulator layout
+  float* part_ml;           // [2*nwg][kWaves][2][3][32] partial max, sum, exact sum
+  unsigned* counters;       // [nrows][2]: arrived, partials written
   int n;
   int heads;
-  float c;          // softmax scale * log2(e)
+  float c;                  // softmax scale * log2(e)
   int nseg;
-  int ntiles;       // total key tiles over all segments
-  int nqt;          // query tiles per head
+  int ntiles;               // tiles per row (T)
+  int nqt;                  // rows per head
+  int nrows;                // heads * nqt
+  int nwg;                  // persistent workgroups
+  long long total;          // nrows * ntiles
   SegArg seg[kMaxSegments];
 };
 
-// swap bits 2 and 3 of a row index
-__device__ __forceinline__ int pi_row(int r) {
-  return (r & ~0xC) | ((r & 4) << 1) | ((r & 8) >> 1);
+// max / sum of a value with the one held by lane ^ 32 (v_permlane32_swap
+// exchanges the two 32-lane halves)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-template <int D>
-__device__ __forceinline__ int swz_k(int row) {
-  return pi_row(row & 15) & (D / 8 - 1);
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ int swz_v(int row) { return (row ^ (row >> 3)) & 7; }
+
+// first step of workgroup w's range, and the owner of step x
+__device__ __forceinline__ long long range_begin(long long w, const AttnArgs& a) {
+  return w * a.total / a.nwg;
+}
+__device__ __forceinline__ int owner_of(long long x, const AttnArgs& a) {
+  return static_cast<int>(((x + 1) * a.nwg - 1) / a.total);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  // address-space casts (generic -> global / LDS) need C-style casts
+  __builtin_amdgcn_global_load_lds((gbl_void*)g, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt low bits [3:0], high
+// bits [15:14]; expcnt [6:4], left at its maximum; lgkmcnt [11:8])
+template <int N>
+__device__ __forceinline__ void wait_vm_keep_lds_done() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+
+// Workgroup barrier without a memory fence (a fence would make the compiler
+// wait for every copy in flight).  Written as an asm statement with a memory
+// clobber so that no memory access is moved across it at any compiler level;
+// it emits no wait of its own.  The caller has already waited for its own LDS
+// accesses and for the copies the next step reads.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("s_barrier" ::: "memory");
+}
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(const AttnArgs a) {
-  constexpr int kKRow = D * 2;                  // bytes per K row in LDS
-  constexpr int kKChunks = D / 8;               // 16-byte chunks per K row
-  constexpr int kKTile = kBk * kKRow;           // bytes of a K tile
-  constexpr int kVTile = D * kBk * 2;           // bytes of a Vt tile (D rows x 128 B)
-  constexpr int kKLoads = kBk * kKChunks / kThreads;   // 16-byte loads per thread
-  constexpr int kVLoads = D * 8 / kThreads;
-  constexpr int kDS = D / 16;                   // MFMA k-steps over d
-  constexpr int kDB = D / 32;                   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2][kKTile + kVTile];
+struct Tile {
+  static constexpr int kKRow = D * 2;             // bytes per K row
+  static constexpr int kKBytes = kBk * kKRow;     // K tile bytes
+  static constexpr int kVBytes = D * kBk * 2;     // Vt tile bytes (D rows of 128 B)
+  static constexpr int kKInstr = kKBytes / 1024 / kWaves;   // 1 KB DMA per wave-instruction
+  static constexpr int kVInstr = kVBytes / 1024 / kWaves;
+};
 
-  const int L = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int h = L / a.nqt;
-  const int qt = L - h * a.nqt;
+// Cursor over one row's key tiles: segment, first key of the tile, and that
+// segment's fields, all wave-uniform (scalar registers).  Moving to the next
+// tile touches no memory except when a segment ends.
+struct TileCursor {
+  int t;                    // tile index within the row
+  int s;                    // segment
+  int k0;                   // first key of the tile within the segment
+  int rows;
+  int pitch;
+  const unsigned char* k;
+  const unsigned char* vt;
+};
+
+__device__ __forceinline__ void cursor_fields(const AttnArgs& a, TileCursor& c) {
+  c.rows = a.seg[c.s].rows;
+  c.pitch = a.seg[c.s].pitch;
+  c.k = a.seg[c.s].k;
+  c.vt = a.seg[c.s].vt;
+}
+__device__ __forceinline__ void cursor_seek(const AttnArgs& a, TileCursor& c, int t) {
+  int s = 0;
+  while (s + 1 < a.nseg && a.seg[s + 1].tile0 <= t) ++s;
+  c.t = t;
+  c.s = s;
+  c.k0 = (t - a.seg[s].tile0) * kBk;
+  cursor_fields(a, c);
+}
+// one tile on, but never past tile `last`
+__device__ __forceinline__ void cursor_next(const AttnArgs& a, TileCursor& c, int last) {
+  if (c.t >= last) return;
+  ++c.t;
+  c.k0 += kBk;
+  if (c.k0 >= c.rows) {
+    ++c.s;
+    c.k0 = 0;
+    cursor_fields(a, c);
+  }
+}
+
+template <int D, bool kLse>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fwd_bf16(const AttnArgs a) {
+  using TL = Tile<D>;
+  constexpr int kDS = D / 16;          // k-steps over d for QK^T
+  constexpr int kDB = D / 32;          // 32-row blocks of O^T
+  // LDS: two K tiles and two Vt tiles, as four separate arrays so that the
+  // compiler can tell reads of one buffer from copies landing in another
+  // (a single array would make it wait for every copy in flight before any
+  // LDS read).  kK0.. name the buffers.
+  constexpr int kK0 = 0, kK1 = 1, kV0 = 2, kV1 = 3;
+  __shared__ __attribute__((aligned(1024))) unsigned char kb0[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb1[TL::kKBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb0[TL::kVBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb1[TL::kVBytes];
+  auto buf = [&](int off) -> unsigned char* {
+    return off == kK0 ? kb0 : off == kK1 ? kb1 : off == kV0 ? vb0 : vb1;
+  };
+  __shared__ unsigned s_ticket;
+
+  const int w = xcd_contiguous(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int qi = qt * kBq + wave * 32 + col;
-  const bool qvalid = qi < a.n;
 
-  // Q^T as B operand: lane holds query qi, features ks*16 + half*8 .. +7
-  bf16x8_t qreg[kDS];
-  {
-    const uint16_t* qrow = a.q + (static_cast<size_t>(qi) * a.heads + h) * D + half * 8;
+  // Per-lane byte offsets of the DMA copies.  K: a 1 KB block holds
+  // 1024 / (2D) consecutive key rows; lane l fills 16-byte chunk l % (D/8) of
+  // row l / (D/8), which takes logical chunk pc ^ (row & 7).  The row's low 3
+  // bits depend on the block only through its parity (D = 128) or not at all
+  // (D = 64).  Vt: a 1 KB block holds 8 rows d of 128 bytes; lane l fills
+  // chunk l % 8 of row l / 8 with logical chunk (l % 8) ^ (l / 8).
+  constexpr int kKLanesPerRow = D / 8;
+  constexpr int kKRowsPerBlk = 1024 / TL::kKRow;
+  uint32_t koff[2];
 #pragma unroll
-    for (int ks = 0; ks < kDS; ++ks) {
-      if (qvalid) {
-        qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qreg[ks][j] = static_cast<__bf16>(0.0f);
-      }
-    }
+  for (int par = 0; par < 2; ++par) {
+    const int row = par * kKRowsPerBlk + lane / kKLanesPerRow;
+    const int pc = lane % kKLanesPerRow;
+    koff[par] = (lane / kKLanesPerRow) * TL::kKRow + ((pc ^ (row & 7)) * 16);
   }
+  const uint32_t vrow = lane >> 3;
+  const uint32_t vchunk16 = (((lane & 7) ^ vrow) & 7) * 16;
 
-  f32x16_t oacc[kDB];
+  // copies of one tile into the LDS buffer at byte offset DST
+  auto dma_k = [&](auto dst_tag, const TileCursor& c, int h) {
+    constexpr int DST = decltype(dst_tag)::value;
+    const unsigned char* base = c.k + (static_cast<size_t>(h) * c.pitch + c.k0) * TL::kKRow;
 #pragma unroll
-  for (int b = 0; b < kDB; ++b)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[b][i] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-
-  uint4 kst[kKLoads], vst[kVLoads];
-  int ls = 0, lk = 0;   // load cursor: segment, first key of the tile
-  int cs = 0, ck = 0;   // compute cursor
-
-  auto load_tile = [&](int s, int k0) {
-    const SegArg g = a.seg[s];
-    const unsigned char* kb = g.k + (static_cast<size_t>(h) * g.pitch + k0) * kKRow;
-#pragma unroll
-    for (int i = 0; i < kKLoads; ++i) {
-      const int c = tid + kThreads * i;
-      kst[i] = ld16(kb + (c / kKChunks) * kKRow + (c % kKChunks) * 16);
-    }
-    const unsigned char* vb = g.vt + (static_cast<size_t>(h) * D * g.pitch + k0) * 2;
-#pragma unroll
-    for (int i = 0; i < kVLoads; ++i) {
-      const int c = tid + kThreads * i;
-      vst[i] = ld16(vb + static_cast<size_t>(c / 8) * g.pitch * 2 + (c % 8) * 16);
+    for (int u = 0; u < TL::kKInstr; ++u) {
+      const int blk = wave * TL::kKInstr + u;
+      dma16(base + blk * 1024 + koff[((blk * kKRowsPerBlk) & 7) / kKRowsPerBlk],
+            buf(DST) + blk * 1024);
     }
   };
-  auto store_tile = [&](int buf) {
-    unsigned char* kl = smem[buf];
-    unsigned char* vl = smem[buf] + kKTile;
+  auto dma_v = [&](auto dst_tag, const TileCursor& c, int h) {
+    constexpr int DST = decltype(dst_tag)::value;
+    const uint32_t pitch2 = static_cast<uint32_t>(c.pitch) * 2;
+    const unsigned char* base = c.vt + static_cast<size_t>(h) * D * pitch2 + c.k0 * 2;
+    const uint32_t voff = vrow * pitch2 + vchunk16;
 #pragma unroll
-    for (int i = 0; i < kKLoads; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / kKChunks;
-      st16(kl + row * kKRow + (((c % kKChunks) ^ swz_k<D>(row)) * 16), kst[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < kVLoads; ++i) {
-      const int c = tid + kThreads * i;
-      const int row = c / 8;
-      st16(vl + row * 128 + (((c % 8) ^ swz_v(row)) * 16), vst[i]);
+    for (int u = 0; u < TL::kVInstr; ++u) {
+      const int blk = wave * TL::kVInstr + u;
+      dma16(base + static_cast<size_t>(blk) * 8 * pitch2 + voff, buf(DST) + blk * 1024);
     }
   };
-  auto advance = [&](int& s, int& k0) {
-    k0 += kBk;
-    if (k0 >= a.seg[s].rows) {
-      ++s;
-      k0 = 0;
-    }
+  auto wait_dma = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
+
+  // K operands of one 32-key half tile: rows kb*32 + col of the K tile at KB
+  auto read_kops = [&](const unsigned char* kl, bf16x8_t (&kops)[kDS]) {
+    const unsigned char* rowp = kl + col * TL::kKRow;
+#pragma unroll
+    for (int ks = 0; ks < kDS; ++ks)
+      kops[ks] = *reinterpret_cast<const bf16x8_t*>(rowp + (((ks * 2 + half) ^ (col & 7)) * 16));
+  };
+  auto qk = [&](const bf16x8_t (&kops)[kDS], const bf16x8_t (&qreg)[2][kDS], f32x16_t (&s)[2]) {
+#pragma unroll
+    for (int cq = 0; cq < 2; ++cq)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[cq][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kDS; ++ks)
+#pragma unroll
+      for (int cq = 0; cq < 2; ++cq)
+        s[cq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kops[ks], qreg[cq][ks], s[cq], 0, 0, 0);
   };
 
-  load_tile(ls, lk);
-  store_tile(0);
-  advance(ls, lk);
-  __syncthreads();
+  for (long long x = range_begin(w, a), xe = range_begin(w + 1, a); x < xe;) {
+    const int r = static_cast<int>(x / a.ntiles);
+    const int t0 = static_cast<int>(x % a.ntiles);
+    const long long rest = xe - x;
+    const int t1 = rest < a.ntiles - t0 ? t0 + static_cast<int>(rest) : a.ntiles;
+    const bool first_piece = x == range_begin(w, a);
+    x += t1 - t0;
+    const int h = r / a.nqt;
+    const int qbase = (r - h * a.nqt) * kBq + wave * kQW;
 
-  for (int j = 0; j < a.ntiles; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < a.ntiles;
-    if (more) load_tile(ls, lk);
-
-    const unsigned char* kl = smem[buf];
-    const unsigned char* vl = smem[buf] + kKTile;
-
-    // ---- S^T = K . Q^T
-    f32x16_t sacc[2];
+    // Q^T as B operand: lane holds query qbase + cq*32 + col, features
+    // ks*16 + half*8 .. +7
+    bf16x8_t qreg[2][kDS];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int cq = 0; cq < 2; ++cq) {
+      const int qi = qbase + cq * 32 + col;
+      const uint16_t* qrow = a.q + (static_cast<size_t>(qi) * a.heads + h) * D + half * 8;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[b][i] = 0.f;
+      for (int ks = 0; ks < kDS; ++ks) {
+        if (qi < a.n) {
+          qreg[cq][ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
+        } else {
 #pragma unroll
-    for (int ks = 0; ks < kDS; ++ks) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int row = b * 32 + pi_row(col);
-        const int chunk = ks * 2 + half;
-        const bf16x8_t kop = *reinterpret_cast<const bf16x8_t*>(
-            kl + row * kKRow + ((chunk ^ swz_k<D>(row)) * 16));
-        sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[ks], sacc[b], 0, 0, 0);
+          for (int j = 0; j < 8; ++j) qreg[cq][ks][j] = static_cast<__bf16>(0.0f);
+        }
       }
     }
 
-    // ---- mask the padded keys of a segment's last tile
-    const int valid = a.seg[cs].rows - ck;
-    if (valid < kBk) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
+    // the scores of one half tile with the padded keys of a segment's last
+    // tile set to -inf; `valid` = keys of this half that exist
+    auto mask = [&](f32x16_t (&sc)[2], int valid) {
+      if (valid < 32) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = b * 32 + pi_row((i >> 2) * 8 + half * 4 + (i & 3));
-          if (key >= valid) sacc[b][i] = -INFINITY;
+          const int key = (i >> 2) * 8 + half * 4 + (i & 3);
+          if (key >= valid) {
+            sc[0][i] = -INFINITY;
+            sc[1][i] = -INFINITY;
+          }
         }
-    }
-
-    // ---- online softmax (base 2, lazy rescale)
-    float mx = sacc[0][0];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[b][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mt = mx * a.c;
-    if (__any(mt > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int b = 0; b < kDB; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[b][i] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float neg_m = -m_run;
-    bf16x8_t pb[4];
-    float lsum = 0.f;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[b][i], a.c, neg_m));
-        lsum += p;
-        pb[b * 2 + (i >> 3)][i & 7] = static_cast<__bf16>(p);
       }
-    l_run += lsum;
-
-    // ---- O^T += Vt . P^T
+    };
+    // scaled max over the 32 keys of a half tile, per query block
+    auto half_max = [&](const f32x16_t (&sc)[2], float (&mt)[2]) {
 #pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {
+      for (int cq = 0; cq < 2; ++cq) {
+        float mx = fmaxf(sc[cq][0], sc[cq][1]);
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const int row = db * 32 + col;
-        const int chunk = ps * 2 + half;
-        const bf16x8_t vop = *reinterpret_cast<const bf16x8_t*>(
-            vl + row * 128 + ((chunk ^ swz_v(row)) * 16));
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[ps], oacc[db], 0, 0, 0);
+        for (int i = 2; i < 16; ++i) mx = fmaxf(mx, sc[cq][i]);
+        mt[cq] = xor32_max(mx) * a.c;
       }
-    }
+    };
 
-    if (more) {
-      store_tile(buf ^ 1);
-      advance(ls, lk);
-    }
-    advance(cs, ck);
-    __syncthreads();
-  }
+    f32x16_t oacc[kDB][2];
+    float m_ref[2] = {0.f, 0.f};
+    float m_seen[2] = {-INFINITY, -INFINITY};
+    float l_run[2];
+    float l_exact[2];                 // exact sums, for the lse output only
+    bool fixed_ref = false;
+    const int tlast = t1 - 1;
+    for (;;) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int cq = 0; cq < 2; ++cq)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[db][cq][i] = 0.f;
+      l_run[0] = l_run[1] = 0.f;
+      l_exact[0] = l_exact[1] = 0.f;
+      f32x16_t sacc[2][2];   // [buffer][cq] scores of a 32-key half tile
 
-  // ---- epilogue: O /= l, store bf16; lse = (m + log2 l) * ln 2
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  if (qvalid) {
-    uint16_t* orow = a.o + (static_cast<size_t>(qi) * a.heads + h) * D;
-#pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint32_t w[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const __bf16 lo = static_cast<__bf16>(oacc[db][g * 4 + 2 * e] * inv);
-          const __bf16 hi = static_cast<__bf16>(oacc[db][g * 4 + 2 * e + 1] * inv);
-          w[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
-                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+      // cursors: tile j (scores, mask), tile j+1 (V copy), tile j+2 (K
+      // copy); the copy cursors stop at the piece's last tile, so every step
+      // issues the same number of copies (the extra ones land in a buffer
+      // that is not read again) and the vmcnt waits stay exact
+      TileCursor cj, cv, ck;
+      cursor_seek(a, cj, t0);
+      cv = cj;
+      cursor_next(a, cv, tlast);
+      ck = cv;
+      cursor_next(a, ck, tlast);
+
+      // ---- prologue: K_t0, V_t0, K_t0+1 in LDS; scores of the first half
+      // tile, which also fix the reference max of the piece
+      __syncthreads();
+      dma_k(std::integral_constant<int, kK0>{}, cj, h);
+      dma_v(std::integral_constant<int, kV0>{}, cj, h);
+      dma_k(std::integral_constant<int, kK1>{}, cv, h);
+      wait_dma();
+      __syncthreads();
+      {
+        bf16x8_t kops[kDS];
+        read_kops(buf(kK0), kops);
+        qk(kops, qreg, sacc[0]);
+      }
+      if (!fixed_ref) {
+        f32x16_t first[2] = {sacc[0][0], sacc[0][1]};
+        mask(first, cj.rows - cj.k0);
+        half_max(first, m_ref);
+      }
+
+      // ---- one pipelined half step.  Half step u = 2i + hh covers keys
+      // [32 hh, 32 hh + 32) of tile j = t0 + i.  It issues the next copies,
+      // reads the operands it needs, computes the scores of half step u+1
+      // while running the softmax of half step u, then adds P V of half step u.
+      auto half_step = [&](auto u_tag) {
+        constexpr int U = decltype(u_tag)::value;     // u mod 4
+        constexpr int HH = U & 1;                      // which half of the tile
+        constexpr int TP = (U >> 1) & 1;               // parity of the tile
+        constexpr int CUR = U & 1;                     // score buffer of this half
+        constexpr int KJ = TP == 0 ? kK0 : kK1;        // K of tile j
+        constexpr int KN = TP == 0 ? kK1 : kK0;        // K of tile j+1
+        constexpr int VJ = TP == 0 ? kV0 : kV1;        // V of tile j
+        constexpr int VN = TP == 0 ? kV1 : kV0;        // V of tile j+1
+        if (HH == 0) {
+          dma_v(std::integral_constant<int, VN>{}, cv, h);   // V_{j+1}; V_{j-1} is done
+        } else {
+          dma_k(std::integral_constant<int, KJ>{}, ck, h);   // K_{j+2}; K_j is done
         }
-        *reinterpret_cast<uint2*>(orow + db * 32 + g * 8 + half * 4) = make_uint2(w[0], w[1]);
+        // operands: K rows of the next half step, Vt columns of this one
+        bf16x8_t kops[kDS];
+        if (HH == 0) {
+          read_kops(buf(KJ) + 32 * TL::kKRow, kops);
+        } else {
+          read_kops(buf(KN), kops);
+        }
+        bf16x8_t vops[2][kDB];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) {
+            const int ps = HH * 2 + pp;
+            vops[pp][db] = *reinterpret_cast<const bf16x8_t*>(
+                buf(VJ) + (db * 32 + col) * 128 + (((ps * 2 + half) ^ (col & 7)) * 16));
+          }
+
+        f32x16_t (&sc)[2] = sacc[CUR];
+        mask(sc, cj.rows - cj.k0 - HH * 32);
+        float mt[2];
+        half_max(sc, mt);
+        m_seen[0] = fmaxf(m_seen[0], mt[0]);
+        m_seen[1] = fmaxf(m_seen[1], mt[1]);
+
+        // scores of the next half step (discarded after the last one)
+        qk(kops, qreg, sacc[1 - CUR]);
+
+        // probabilities as bf16 P^T, and their row sums taken over the
+        // rounded values the PV product uses (so O is an exact convex
+        // combination of the weights applied): bf16 pairs dotted with (1, 1)
+        bf16x8_t pb[2][2];
+        const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+        for (int cq = 0; cq < 2; ++cq) {
+          const float neg_m = -m_ref[cq];
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            pb[cq][i >> 3][i & 7] =
+                static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sc[cq][i], a.c, neg_m)));
+          float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const bf16x8_t v = pb[cq][g];
+            acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), ones, acc0, false);
+            acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), ones, acc1, false);
+            acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), ones, acc0, false);
+            acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, acc1, false);
+          }
+          l_run[cq] += acc0 + acc1;
+          if constexpr (kLse) {
+            // the log-sum-exp output wants the exact sum of the unrounded p
+            float p[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[cq][i], a.c, neg_m));
+#pragma unroll
+            for (int st = 8; st >= 1; st >>= 1)
+#pragma unroll
+              for (int i = 0; i < st; ++i) p[i] += p[i + st];
+            l_exact[cq] += p[0];
+          }
+        }
+
+        // O^T += Vt . P^T over these 32 keys
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int db = 0; db < kDB; ++db)
+#pragma unroll
+            for (int cq = 0; cq < 2; ++cq)
+              oacc[db][cq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vops[pp][db], pb[cq][pp],
+                                                                    oacc[db][cq], 0, 0, 0);
+        // the copies issued one half step earlier must have landed (the ones
+        // just issued, of the other kind, may stay in flight) and this wave's
+        // LDS reads must be done before any wave starts overwriting buffers
+        if (HH == 0) {
+          wait_vm_keep_lds_done<TL::kVInstr>();
+        } else {
+          wait_vm_keep_lds_done<TL::kKInstr>();
+        }
+        barrier_no_fence();
+        if (HH == 1) {
+          cursor_next(a, cj, tlast);
+          cursor_next(a, cv, tlast);
+          cursor_next(a, ck, tlast);
+        }
+      };
+
+      for (int j = t0; j < t1; j += 2) {
+        half_step(std::integral_constant<int, 0>{});
+        half_step(std::integral_constant<int, 1>{});
+        if (j + 1 < t1) {
+          half_step(std::integral_constant<int, 2>{});
+          half_step(std::integral_constant<int, 3>{});
+        }
       }
-    if (a.lse && half == 0) {
-      a.lse[static_cast<size_t>(h) * a.n + qi] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+      // a logit too far above the reference: compute the piece again with
+      // the largest logit as reference (then no p exceeds 1)
+      if (fixed_ref || !__any(m_seen[0] > m_ref[0] + kRefMargin ||
+                              m_seen[1] > m_ref[1] + kRefMargin))
+        break;
+      m_ref[0] = m_seen[0];
+      m_ref[1] = m_seen[1];
+      fixed_ref = true;
+    }
+    float m_run[2] = {m_ref[0], m_ref[1]};
+
+    // ---- finish the piece
+    float l_tot[2], le_tot[2];
+#pragma unroll
+    for (int cq = 0; cq < 2; ++cq) {
+      l_tot[cq] = xor32_sum(l_run[cq]);
+      le_tot[cq] = kLse ? xor32_sum(l_exact[cq]) : 0.f;
+    }
+
+    const long long rs = static_cast<long long>(r) * a.ntiles;
+    const int w_lo = owner_of(rs, a);
+    const int w_hi = owner_of(rs + a.ntiles - 1, a);
+    bool write_final = true;
+    if (w_hi > w_lo) {
+      // this row is split: the last piece to arrive merges the others
+      unsigned* arrived = a.counters + 2 * r;
+      unsigned* written = arrived + 1;
+      const unsigned npieces = static_cast<unsigned>(w_hi - w_lo + 1);
+      __syncthreads();
+      if (tid == 0)
+        s_ticket = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const bool last = s_ticket == npieces - 1;
+      const int slot = first_piece ? 0 : 1;
+      if (!last) {
+        write_final = false;
+        float* po = a.part_o + (static_cast<size_t>(2 * w + slot) * kBq * D) +
+                    static_cast<size_t>(wave) * kQW * D;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int cq = 0; cq < 2; ++cq)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) po[((db * 2 + cq) * 16 + i) * 64 + lane] = oacc[db][cq][i];
+        float* pml = a.part_ml + (static_cast<size_t>(2 * w + slot) * kWaves + wave) * kMlPerWave;
+        if (half == 0) {
+#pragma unroll
+          for (int cq = 0; cq < 2; ++cq) {
+            pml[(cq * 3 + 0) * 32 + col] = m_run[cq];
+            pml[(cq * 3 + 1) * 32 + col] = l_tot[cq];
+            pml[(cq * 3 + 2) * 32 + col] = le_tot[cq];
+          }
+        }
+        __threadfence();
+        __syncthreads();
+        if (tid == 0)
+          __hip_atomic_fetch_add(written, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        // wait until every other piece has stored its partial (they have all
+        // arrived already, so this is a short wait), then merge
+        if (tid == 0) {
+          for (int spin = 0; spin < (1 << 26); ++spin) {
+            if (__hip_atomic_load(written, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >=
+                npieces - 1)
+              break;
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+        __syncthreads();
+        __threadfence();
+        for (int ow = w_lo; ow <= w_hi; ++ow) {
+          if (ow == w) continue;
+          const int oslot = range_begin(ow, a) >= rs ? 0 : 1;
+          const float* po = a.part_o + (static_cast<size_t>(2 * ow + oslot) * kBq * D) +
+                            static_cast<size_t>(wave) * kQW * D;
+          const float* pml =
+              a.part_ml + (static_cast<size_t>(2 * ow + oslot) * kWaves + wave) * kMlPerWave;
+#pragma unroll
+          for (int cq = 0; cq < 2; ++cq) {
+            const float mo = pml[(cq * 3 + 0) * 32 + col];
+            const float lo = pml[(cq * 3 + 1) * 32 + col];
+            const float leo = pml[(cq * 3 + 2) * 32 + col];
+            const float m_new = fmaxf(m_run[cq], mo);
+            const float as = __builtin_amdgcn_exp2f(m_run[cq] - m_new);
+            const float ao = __builtin_amdgcn_exp2f(mo - m_new);
+#pragma unroll
+            for (int db = 0; db < kDB; ++db)
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                oacc[db][cq][i] = oacc[db][cq][i] * as + po[((db * 2 + cq) * 16 + i) * 64 + lane] * ao;
+            l_tot[cq] = l_tot[cq] * as + lo * ao;
+            le_tot[cq] = le_tot[cq] * as + leo * ao;
+            m_run[cq] = m_new;
+          }
+        }
+        if (tid == 0) {
+          __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(written, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+
+    if (write_final) {
+#pragma unroll
+      for (int cq = 0; cq < 2; ++cq) {
+        const int qi = qbase + cq * 32 + col;
+        if (qi >= a.n) continue;
+        const float inv = 1.0f / l_tot[cq];
+        uint16_t* orow = a.o + (static_cast<size_t>(qi) * a.heads + h) * D;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint32_t wv[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const __bf16 lo = static_cast<__bf16>(oacc[db][cq][g * 4 + 2 * e] * inv);
+              const __bf16 hi = static_cast<__bf16>(oacc[db][cq][g * 4 + 2 * e + 1] * inv);
+              wv[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+            }
+            *reinterpret_cast<uint2*>(orow + db * 32 + g * 8 + half * 4) = make_uint2(wv[0], wv[1]);
+          }
+        if (kLse && half == 0)
+          a.lse[static_cast<size_t>(h) * a.n + qi] = (m_run[cq] + __log2f(le_tot[cq])) * kLn2;
+      }
     }
   }
+}
+
+__global__ void fill_u32(unsigned* p, int n, unsigned v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
 }
 
 template <int D>
@@ -290,19 +649,43 @@ kvc_status launch_bf16(const AttnDesc& d, hipStream_t stream) {
   a.heads = d.heads;
   a.c = d.scale * 1.4426950408889634f;
   a.nseg = d.nseg;
-  a.ntiles = 0;
+  int tiles = 0;
   for (int s = 0; s < d.nseg; ++s) {
+    if (d.seg[s].rows <= 0 || d.seg[s].pitch < d.seg[s].rows || d.seg[s].pitch % kBk)
+      return KVC_E_INVAL;
     a.seg[s].k = static_cast<const unsigned char*>(d.seg[s].k);
     a.seg[s].vt = static_cast<const unsigned char*>(d.seg[s].vt);
     a.seg[s].rows = d.seg[s].rows;
     a.seg[s].pitch = d.seg[s].pitch;
-    if (d.seg[s].rows <= 0 || d.seg[s].pitch < d.seg[s].rows || d.seg[s].pitch % kBk)
-      return KVC_E_INVAL;
-    a.ntiles += (d.seg[s].rows + kBk - 1) / kBk;
+    a.seg[s].tile0 = tiles;
+    a.seg[s].pad_ = 0;
+    tiles += (d.seg[s].rows + kBk - 1) / kBk;
   }
+  a.ntiles = tiles;
   a.nqt = (d.n + kBq - 1) / kBq;
-  const int nblk = a.nqt * d.heads;
-  hipLaunchKernelGGL(attn_fwd_bf16<D>, dim3(nblk), dim3(kThreads), 0, stream, a);
+  a.nrows = a.nqt * d.heads;
+  a.total = static_cast<long long>(a.nrows) * a.ntiles;
+  const long long slots = std::min(2 * device_cus(), kMaxWg);
+  const long long by_size = std::max<long long>(1, a.total / kMinPieceTiles);
+  a.nwg = static_cast<int>(std::min(slots, std::max<long long>(by_size, 1)));
+  // workspace: counters, then partial max/sum, then partial O
+  unsigned char* ws = static_cast<unsigned char*>(d.workspace);
+  const size_t cnt_bytes = align_up(sizeof(unsigned) * 2 * a.nrows, 256);
+  const size_t ml_bytes = align_up(sizeof(float) * 2 * kMaxWg * kWaves * kMlPerWave, 256);
+  const size_t po_bytes = sizeof(float) * 2 * kMaxWg * kBq * D;
+  if (d.workspace_bytes < cnt_bytes + ml_bytes + po_bytes) return KVC_E_INVAL;
+  a.counters = reinterpret_cast<unsigned*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + cnt_bytes);
+  a.part_o = reinterpret_cast<float*>(ws + cnt_bytes + ml_bytes);
+  if (!d.workspace_ready) {
+    const int nc = 2 * a.nrows;
+    hipLaunchKernelGGL(fill_u32, dim3((nc + 255) / 256), dim3(256), 0, stream, a.counters, nc,
+                       0u);
+  }
+  if (a.lse)
+    hipLaunchKernelGGL((attn_fwd_bf16<D, true>), dim3(a.nwg), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16<D, false>), dim3(a.nwg), dim3(kThreads), 0, stream, a);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_DEVICE;
 }
 

@@ -1,7 +1,10 @@
 // K1: fused cache write.  Moves a chunk's K/V from the caller's token-major
 // layout [rows][H][d] into a ring slot: K head-major [H][pitch][d] and V
 // transposed per head [H][d][pitch] (the layout the attention kernel's PV
-// product reads), zero-filling the padded rows.  The fp8 variant quantises to
+// product reads), zero-filling the padded rows.  Within every group of 16
+// keys the V columns are stored in the order kappa (swap of key-index bits 2
+// and 3), which is the order in which the attention kernel's score
+// accumulator hands keys to the PV product.  The fp8 variant quantises to
 // E4M3 with one float32 scale per (head, slot).
 //
 // The cached state is the clean K/V of each generated chunk, kept for the
@@ -20,6 +23,11 @@ namespace {
 
 constexpr int kRowsPerBlock = kTileKeys;   // 64
 constexpr int kThreads = 256;
+
+// key stored in V column p of a tile: swap bits 2 and 3 (an involution)
+__device__ __forceinline__ int kappa(int p) {
+  return (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
 
 // ---------------------------------------------------------------- bf16 ----
 
@@ -61,8 +69,8 @@ __global__ __launch_bounds__(kThreads) void cache_write_bf16(
     uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = vtile[(ch * 8 + 2 * j) * kLdsPitch + dd];
-      const uint32_t hi = vtile[(ch * 8 + 2 * j + 1) * kLdsPitch + dd];
+      const uint32_t lo = vtile[kappa(ch * 8 + 2 * j) * kLdsPitch + dd];
+      const uint32_t hi = vtile[kappa(ch * 8 + 2 * j + 1) * kLdsPitch + dd];
       w[j] = lo | (hi << 16);
     }
     st16(vtd + (static_cast<size_t>(h) * D + dd) * pitch + r0 + ch * 8,
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
       uint32_t x = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        x |= static_cast<uint32_t>(vtile[(ch * 16 + 4 * j + b) * kLdsPitch + dd]) << (8 * b);
+        x |= static_cast<uint32_t>(vtile[kappa(ch * 16 + 4 * j + b) * kLdsPitch + dd]) << (8 * b);
       w[j] = x;
     }
     st16(vtd + (static_cast<size_t>(h) * D + dd) * pitch + r0 + ch * 16,

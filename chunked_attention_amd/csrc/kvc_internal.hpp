@@ -14,6 +14,13 @@ namespace kvc {
 constexpr int kMaxSegments = KVC_MAX_WINDOW + 3;   // cond + sink + W + current
 constexpr int kTileKeys = KVC_TILE_KEYS;
 
+// Attention work decomposition (shared by the launcher and the workspace
+// sizing): a row is kAttnRowQueries queries of one head, run by kAttnWaves
+// waves; at most kAttnMaxWg persistent workgroups split the rows' key tiles.
+constexpr int kAttnWaves = 2;
+constexpr int kAttnRowQueries = 128;
+constexpr int kAttnMaxWg = 512;
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int pad_rows(int r) { return (r + kTileKeys - 1) / kTileKeys * kTileKeys; }
 
@@ -66,6 +73,7 @@ struct AttnDesc {
   AttnSegment seg[kMaxSegments];
   void* workspace = nullptr;    // device scratch for split partials
   size_t workspace_bytes = 0;
+  bool workspace_ready = false; // counters in the workspace already zeroed
 };
 
 // Launchers.  Return KVC_OK or KVC_E_DEVICE / KVC_E_UNSUPPORTED.  The device

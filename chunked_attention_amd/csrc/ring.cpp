@@ -105,6 +105,7 @@ struct kvc_ring {
   int staging;            // staging slot in phase STAGED, -1 otherwise
   int current;            // slot of the current chunk (STAGED or COMMITTED)
   int cond_valid;
+  int work_ready;         // attention workspace counters initialised
 };
 
 namespace kvc {
@@ -277,7 +278,10 @@ kvc_status chunk_attn_fwd(kvc_ring* r, const void* q, void* o, float* lse, void*
   d.scale = r->scale;
   d.workspace = r->base + r->L.work_off;
   d.workspace_bytes = r->L.work_bytes;
-  return launch_attention(d, stream);
+  d.workspace_ready = r->work_ready != 0;
+  kvc_status s = launch_attention(d, stream);
+  if (s == KVC_OK) r->work_ready = 1;
+  return s;
 }
 
 kvc_status kvc_evict(kvc_ring* r, int32_t* evicted) {

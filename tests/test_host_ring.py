@@ -109,6 +109,10 @@ def expected_bytes(H, d, n, m, W, e, fp8):
     total = (slot(m) if m else 0) + (W + 2) * slot(n)
     if fp8:
         total += al(4 * 2 * H * (P(max(n, m)) // 64))
+    # attention workspace: 2 counters per 128-query row, then 2 partial slots
+    # per persistent workgroup (512 at most): max + 2 sums and fp32 O [128][d]
+    rows = H * ((n + 127) // 128)
+    total += al(8 * rows) + al(4 * 2 * 512 * 3 * 128) + 4 * 2 * 512 * 128 * d
     return total
 
 
@@ -122,9 +126,10 @@ def test_required_bytes_matches_layout(lib, H, d, n, m, W, fp8):
 
 
 def test_720p_ring_size():
-    # 720p bf16: cond 256 rows + 5 slots of 1620 rows (padded to 1664), 40 heads
+    # 720p bf16: cond 256 rows + 5 slots of 1620 rows (padded to 1664), 40
+    # heads, plus the attention workspace (520 rows; 512 workgroups x 2 slots)
     assert expected_bytes(40, 128, 1620, 256, 3, 2, False) == \
-        2 * 40 * 128 * 2 * (256 + 5 * 1664)
+        2 * 40 * 128 * 2 * (256 + 5 * 1664) + 4352 + 1572864 + 67108864
 
 
 @pytest.mark.parametrize("bad", [
