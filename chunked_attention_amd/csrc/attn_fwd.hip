@@ -520,12 +520,15 @@ void attn_fwd_bf16(const AttnArgs a) {
       const unsigned npieces = static_cast<unsigned>(w_hi - w_lo + 1);
       __syncthreads();
       if (tid == 0)
-        s_ticket = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_ticket = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
       const bool last = s_ticket == npieces - 1;
       const int slot = first_piece ? 0 : 1;
       if (!last) {
         write_final = false;
+        // Partials are written and read with device-scope relaxed atomics
+        // (write-through, coherent across the XCDs' L2s), ordered by waiting
+        // for completion before the counter update: no cache writeback needed.
         float* po = a.part_o + (static_cast<size_t>(2 * w + slot) * kBq * D) +
                     static_cast<size_t>(wave) * kQW * D;
 #pragma unroll
@@ -533,35 +536,73 @@ void attn_fwd_bf16(const AttnArgs a) {
 #pragma unroll
           for (int cq = 0; cq < 2; ++cq)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) po[((db * 2 + cq) * 16 + i) * 64 + lane] = oacc[db][cq][i];
+            for (int i = 0; i < 16; ++i)
+              __hip_atomic_store(po + ((db * 2 + cq) * 16 + i) * 64 + lane, oacc[db][cq][i],
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         float* pml = a.part_ml + (static_cast<size_t>(2 * w + slot) * kWaves + wave) * kMlPerWave;
         if (half == 0) {
 #pragma unroll
           for (int cq = 0; cq < 2; ++cq) {
-            pml[(cq * 3 + 0) * 32 + col] = m_run[cq];
-            pml[(cq * 3 + 1) * 32 + col] = l_tot[cq];
-            pml[(cq * 3 + 2) * 32 + col] = le_tot[cq];
+            __hip_atomic_store(pml + (cq * 3 + 0) * 32 + col, m_run[cq], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pml + (cq * 3 + 1) * 32 + col, l_tot[cq], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pml + (cq * 3 + 2) * 32 + col, le_tot[cq], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
           }
         }
-        __threadfence();
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): stores complete
         __syncthreads();
         if (tid == 0)
-          __hip_atomic_fetch_add(written, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(written, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       } else {
         // wait until every other piece has stored its partial (they have all
         // arrived already, so this is a short wait), then merge
         if (tid == 0) {
           for (int spin = 0; spin < (1 << 26); ++spin) {
-            if (__hip_atomic_load(written, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >=
+            if (__hip_atomic_load(written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
                 npieces - 1)
               break;
             __builtin_amdgcn_s_sleep(1);
           }
         }
+        wait_dma();
         __syncthreads();
-        __threadfence();
+        // Merge in piece order whoever merges, so the result is bitwise the
+        // same from run to run: sum_i O_i 2^(m_i - m_max), starting from the
+        // first piece.  This wave's own partial waits in LDS (its tile
+        // buffers are idle now: no copy is in flight after the loop).
+        unsigned char* own0 = wave == 0 ? buf(kK0) : buf(kV0);
+        unsigned char* own1 = wave == 0 ? buf(kK1) : buf(kV1);
+        auto own_at = [&](int db, int cq, int i) -> float* {
+          unsigned char* base = db < kDB / 2 ? own0 : own1;
+          const int dbl = db < kDB / 2 ? db : db - kDB / 2;
+          return reinterpret_cast<float*>(base) + ((dbl * 2 + cq) * 16 + i) * 64 + lane;
+        };
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int cq = 0; cq < 2; ++cq)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) *own_at(db, cq, i) = oacc[db][cq][i];
+        float mmax[2] = {m_run[0], m_run[1]};
         for (int ow = w_lo; ow <= w_hi; ++ow) {
           if (ow == w) continue;
+          const int oslot = range_begin(ow, a) >= rs ? 0 : 1;
+          const float* pml =
+              a.part_ml + (static_cast<size_t>(2 * ow + oslot) * kWaves + wave) * kMlPerWave;
+#pragma unroll
+          for (int cq = 0; cq < 2; ++cq)
+            mmax[cq] = fmaxf(mmax[cq], __hip_atomic_load(pml + (cq * 3 + 0) * 32 + col,
+                                                         __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT));
+        }
+        const float own_m[2] = {m_run[0], m_run[1]};
+        const float own_l[2] = {l_tot[0], l_tot[1]};
+        const float own_le[2] = {le_tot[0], le_tot[1]};
+        for (int ow = w_lo; ow <= w_hi; ++ow) {
+          const bool mine = ow == w;
+          const bool first = ow == w_lo;
           const int oslot = range_begin(ow, a) >= rs ? 0 : 1;
           const float* po = a.part_o + (static_cast<size_t>(2 * ow + oslot) * kBq * D) +
                             static_cast<size_t>(wave) * kQW * D;
@@ -569,22 +610,36 @@ void attn_fwd_bf16(const AttnArgs a) {
               a.part_ml + (static_cast<size_t>(2 * ow + oslot) * kWaves + wave) * kMlPerWave;
 #pragma unroll
           for (int cq = 0; cq < 2; ++cq) {
-            const float mo = pml[(cq * 3 + 0) * 32 + col];
-            const float lo = pml[(cq * 3 + 1) * 32 + col];
-            const float leo = pml[(cq * 3 + 2) * 32 + col];
-            const float m_new = fmaxf(m_run[cq], mo);
-            const float as = __builtin_amdgcn_exp2f(m_run[cq] - m_new);
-            const float ao = __builtin_amdgcn_exp2f(mo - m_new);
+            float mo, lo, leo;
+            if (mine) {
+              mo = own_m[cq];
+              lo = own_l[cq];
+              leo = own_le[cq];
+            } else {
+              mo = __hip_atomic_load(pml + (cq * 3 + 0) * 32 + col, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+              lo = __hip_atomic_load(pml + (cq * 3 + 1) * 32 + col, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+              leo = __hip_atomic_load(pml + (cq * 3 + 2) * 32 + col, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+            }
+            const float f = __builtin_amdgcn_exp2f(mo - mmax[cq]);
 #pragma unroll
             for (int db = 0; db < kDB; ++db)
 #pragma unroll
-              for (int i = 0; i < 16; ++i)
-                oacc[db][cq][i] = oacc[db][cq][i] * as + po[((db * 2 + cq) * 16 + i) * 64 + lane] * ao;
-            l_tot[cq] = l_tot[cq] * as + lo * ao;
-            le_tot[cq] = le_tot[cq] * as + leo * ao;
-            m_run[cq] = m_new;
+              for (int i = 0; i < 16; ++i) {
+                const float v = mine ? *own_at(db, cq, i)
+                                     : __hip_atomic_load(po + ((db * 2 + cq) * 16 + i) * 64 + lane,
+                                                         __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+                oacc[db][cq][i] = first ? v * f : fmaf(v, f, oacc[db][cq][i]);
+              }
+            l_tot[cq] = first ? lo * f : fmaf(lo, f, l_tot[cq]);
+            le_tot[cq] = first ? leo * f : fmaf(leo, f, le_tot[cq]);
           }
         }
+        m_run[0] = mmax[0];
+        m_run[1] = mmax[1];
         if (tid == 0) {
           __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(written, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
