@@ -17,7 +17,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import statistics
 import sys
@@ -36,7 +35,8 @@ def attn_flops(w, kv_len: int) -> float:
 
 
 def cpu_baseline(w, seconds: float, seed_dist: str = "baseline") -> dict:
-    """The fp64 oracle on a bounded sample of the steady-state chunk."""
+    """The fp64 oracle on a bounded sample of the steady-state chunk: the
+    whole call (all heads) repeated until about `seconds` of CPU time."""
     import numpy as np
     import synth
     from oracle import attention as O1
@@ -52,30 +52,30 @@ def cpu_baseline(w, seconds: float, seed_dist: str = "baseline") -> dict:
     hist = [s.kv_clean(j) for j in ids]
     k, v = s.kv_noisy(t)
     q = s.q(t)
-    f64 = lambda x, hs: O1.as_f64(x)[:, hs]
+    f64 = O1.as_f64
+    args = (f64(q), f64(ck), f64(cv), [f64(a) for a, _ in hist], [f64(b) for _, b in hist],
+            f64(k), f64(v), w.scale)
 
-    def run(hs):
-        t0 = time.perf_counter()
-        O1.chunk_attention(f64(q, hs), f64(ck, hs), f64(cv, hs),
-                           [f64(a, hs) for a, _ in hist], [f64(b, hs) for _, b in hist],
-                           f64(k, hs), f64(v, hs), w.scale)
-        return time.perf_counter() - t0
-
-    one = run([0])
-    nh = int(max(1, min(w.heads, seconds / max(one, 1e-3))))
-    hs = list(range(nh))
-    dt = run(hs)
+    t0 = time.perf_counter()
+    O1.chunk_attention(*args)
+    one = time.perf_counter() - t0
+    reps = max(1, int(round(seconds / max(one, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(reps - 1):
+        O1.chunk_attention(*args)
+    dt = one + time.perf_counter() - t0
     kv_len = O1.kv_length(t, w.cond_tokens, w.chunk_tokens, w.window)
-    flops = 4.0 * w.chunk_tokens * kv_len * w.head_dim * nh
+    flops = 4.0 * w.chunk_tokens * kv_len * w.head_dim * w.heads * reps
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{w.name} steady chunk t={t} ({kv_len} keys), heads 0..{nh - 1} of "
-                  f"{w.heads}, fp64 numpy oracle incl. explicit KV concatenation, "
-                  f"{dt:.2f} s; implied {nh / w.heads / dt:.4f} chunks/s",
+        "sample": f"{w.name} steady chunk t={t} ({kv_len} keys, all {w.heads} heads), "
+                  f"fp64 numpy oracle incl. explicit KV concatenation, {reps} calls in "
+                  f"{dt:.2f} s; {reps / dt:.4f} chunks/s",
         "seconds": dt,
+        "calls": reps,
         "cpu_model": _cpu_model(),
         "affinity_cores": len(os.sched_getaffinity(0)),
     }
@@ -107,7 +107,12 @@ class Inputs:
         self.pool = pool
 
 
-def run_stream_bench(w, args, device):
+def run_stream_bench(w, args, device, flat: bool):
+    """Streams chunks through `w.layers` rings.  The window is filled first
+    (untimed); then `warmup` untimed and `steps` timed steady-state chunks,
+    or, with `flat`, every chunk from the first full window to the end of
+    the stream, timed one by one."""
+    import gc
     import torch
     import chunked_attention_amd as kv
     from oracle.attention import kv_length
@@ -121,16 +126,26 @@ def run_stream_bench(w, args, device):
         for r in rings:
             r.cond(*inp.cond)
     stream = torch.cuda.current_stream()
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    attn_events = []
-    write_events = []
+
+    if flat:
+        warmup, steps = 0, w.chunks - (w.window + 1)
+    else:
+        warmup, steps = args.warmup, args.steps
+    per_step = w.steps * w.layers * 3 + w.layers * 2 + 1
+    pool_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * per_step + 2)]
+    ev_iter = iter(pool_ev)
+    attn_events, write_events, step_events = [], [], []
 
     def chunk(t: int, timed: bool):
         c = t % pool
+        if timed:
+            e = next(ev_iter)
+            e.record(stream)
+            step_events.append(e)
         for st in range(w.steps):
             for li, r in enumerate(rings):
                 if timed:
-                    e0, e1, e2 = ev(), ev(), ev()
+                    e0, e1, e2 = next(ev_iter), next(ev_iter), next(ev_iter)
                     e0.record(stream)
                     r.stage(*inp.noisy[c][st])
                     e1.record(stream)
@@ -143,7 +158,7 @@ def run_stream_bench(w, args, device):
                     r.attention(inp.q[c][st], out=outs[li & 1])
         for r in rings:
             if timed:
-                e0, e1 = ev(), ev()
+                e0, e1 = next(ev_iter), next(ev_iter)
                 e0.record(stream)
                 r.commit(*inp.clean[c])
                 e1.record(stream)
@@ -152,45 +167,81 @@ def run_stream_bench(w, args, device):
                 r.commit(*inp.clean[c])
             r.evict()
 
-    # fill the window (untimed) so every step is a steady-state chunk
+    # fill the window (untimed) so every timed step is a steady-state chunk
     t = 0
     while t <= w.window:
         chunk(t, False)
         t += 1
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         chunk(t, False)
         t += 1
     torch.cuda.synchronize()
     t_first = t
-    start, end = ev(), ev()
-    step_events = []
-    start.record(stream)
-    for _ in range(args.steps):
-        e = ev()
-        e.record(stream)
-        step_events.append(e)
-        chunk(t, True)
-        t += 1
-    end.record(stream)
-    torch.cuda.synchronize()
+    start, end = next(ev_iter), next(ev_iter)
+    # the timed region is host-driven: keep Python's collector from pausing
+    # the launches (the GPU would idle behind it)
+    gc.collect()
+    gc.disable()
+    try:
+        start.record(stream)
+        for _ in range(steps):
+            chunk(t, True)
+            t += 1
+        end.record(stream)
+        torch.cuda.synchronize()
+    finally:
+        gc.enable()
     total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    attn_ms = [a.elapsed_time(b) for a, b in attn_events]
-    write_ms = [a.elapsed_time(b) for a, b in write_events]
     step_ms = [step_events[i].elapsed_time(step_events[i + 1])
-               for i in range(len(step_events) - 1)] + \
-        [step_events[-1].elapsed_time(end)]
-    kv_len = kv_length(t_first, w.cond_tokens, w.chunk_tokens, w.window)
-    return {
-        "ms_per_step": ms_step,
-        "attn_ms": attn_ms,
-        "write_ms": write_ms,
+               for i in range(len(step_events) - 1)] + [step_events[-1].elapsed_time(end)]
+    res = {
+        "ms_per_step": total_ms / steps,
+        "steps": steps,
+        "warmup": warmup,
+        "attn_ms": [a.elapsed_time(b) for a, b in attn_events],
+        "write_ms": [a.elapsed_time(b) for a, b in write_events],
         "step_ms": step_ms,
-        "kv_len": kv_len,
+        "kv_len": kv_length(t_first, w.cond_tokens, w.chunk_tokens, w.window),
         "first_chunk": t_first,
+        "last_chunk": t - 1,
         "calls_per_step": w.steps * w.layers,
         "writes_per_step": (w.steps + 1) * w.layers,
     }
+    if args.copy_calib_mib:
+        # a plain device copy of known size, for scaling the HBM byte counters
+        # (an elementwise negation: reads and writes nbytes once each)
+        nbytes = args.copy_calib_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=device)
+        dst = torch.empty_like(src)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.neg(src, out=dst)
+        c0.record(stream)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        res["copy_calib"] = {"bytes_each_way": nbytes,
+                             "gbps": 2 * nbytes * 3 / (c0.elapsed_time(c1) * 1e-3) / 1e9}
+    return res
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_720p_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "chunked_attention_amd", "csrc", "attn_fwd.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the attention kernel from the committed
+    counter summary, or None if there is none or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def main() -> int:
@@ -203,6 +254,8 @@ def main() -> int:
     ap.add_argument("--pool", type=int, default=16, help="distinct input chunks uploaded")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -221,28 +274,33 @@ def main() -> int:
     w = synth.WORKLOADS[args.config]
     if args.config == "depth":
         args.pool = min(args.pool, 4)
+        args.steps = min(args.steps, 20)
+        args.warmup = min(args.warmup, 2)
+    flat = args.config == "long"
 
-    r = run_stream_bench(w, args, device)
+    r = run_stream_bench(w, args, device, flat)
     flops = attn_flops(w, r["kv_len"])
     step_s = r["ms_per_step"] / 1e3
     attn_us = statistics.mean(r["attn_ms"]) * 1e3
     attn_med_us = statistics.median(r["attn_ms"]) * 1e3
-    write_us = statistics.mean(r["write_ms"]) * 1e3
+    write_us = statistics.median(r["write_ms"]) * 1e3
     fp8 = w.kv_dtype != "bf16"
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     achieved = flops / (attn_us * 1e-6) / 1e12
     e = 1 if fp8 else 2
     write_bytes = 2 * w.chunk_tokens * w.heads * w.head_dim * (2 + e)   # read bf16 K,V + write
     value = flops * r["calls_per_step"] / step_s / 1e12
-    steady = r["step_ms"]
-    med = statistics.median(steady)
+    steps_ms = r["step_ms"]
+    med = statistics.median(steps_ms)
+    dev = lambda xs, m: round(100 * max(abs(x - m) for x in xs) / m, 2)
+    traffic = measured_traffic() if (w.name == "720p" and not fp8) else None
     out = {
         "metric": "chunk-attn TFLOP/s + chunks/s at 720p chunk shape; % of MFMA peak",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": r["steps"],
+        "warmup": r["warmup"],
         "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -252,8 +310,9 @@ def main() -> int:
         "config": {
             "workload": f"{w.name}: H={w.heads} d={w.head_dim} n={w.chunk_tokens} "
                         f"m={w.cond_tokens} W={w.window} layers={w.layers} steps={w.steps}, "
-                        f"steady-state chunks (|S|={r['kv_len']} keys) from chunk "
-                        f"{r['first_chunk']}",
+                        f"steady-state chunks {r['first_chunk']}..{r['last_chunk']} "
+                        f"(|S|={r['kv_len']} keys); one step = STAGE + attention per "
+                        f"denoise step and layer, COMMIT + evict per layer",
             "heads": w.heads, "head_dim": w.head_dim, "chunk_tokens": w.chunk_tokens,
             "cond_tokens": w.cond_tokens, "window": w.window, "kv_len": r["kv_len"],
             "layers": w.layers, "denoise_steps": w.steps, "kv_dtype": w.kv_dtype,
@@ -262,22 +321,47 @@ def main() -> int:
         "pct_mfma_peak": round(100 * value / peak, 2),
         "attn_kernel_us": round(attn_us, 2),
         "attn_kernel_median_us": round(attn_med_us, 2),
+        "attn_calls_per_s": round(1e6 / attn_us, 1),
         "attn_gflop_per_call": round(flops / 1e9, 3),
-        "cache_write_us": round(write_us, 2),
+        "cache_write_median_us": round(write_us, 2),
         "cache_write_gbps": round(write_bytes / (write_us * 1e-6) / 1e9, 1),
         "step_ms_median": round(med, 4),
-        "step_ms_max_dev_pct": round(100 * max(abs(x - med) for x in steady) / med, 2),
+        "step_ms_max_dev_pct": dev(steps_ms, med),
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
-            "kernel": "attn_fwd_bf16<128>" if not fp8 else "attn_fwd_fp8<128>",
+            "traffic": traffic,
+            "kernel": f"attn_fwd_bf16<{w.head_dim},1,false>" if not fp8 else
+                      f"attn_fwd_fp8<{w.head_dim}>",
             "per_launch_flops": flops,
         },
     }
+    if flat:
+        per_call = r["attn_ms"]
+        am = statistics.median(per_call)
+        k = max(1, len(steps_ms) // 10)
+        q95 = lambda xs, m: round(100 * sorted(abs(x - m) for x in xs)[int(0.95 * (len(xs) - 1))]
+                                  / m, 2)
+        out["flatness"] = {
+            "chunks": [r["first_chunk"], r["last_chunk"]],
+            "step_ms_median": round(med, 4),
+            "step_ms_max_dev_pct": dev(steps_ms, med),
+            "step_ms_p95_dev_pct": q95(steps_ms, med),
+            "step_ms_drift_pct": round(100 * (statistics.median(steps_ms[-k:]) -
+                                              statistics.median(steps_ms[:k])) / med, 2),
+            "attn_us_median": round(am * 1e3, 2),
+            "attn_max_dev_pct": dev(per_call, am),
+            "attn_p95_dev_pct": q95(per_call, am),
+            "attn_drift_pct": round(100 * (statistics.median(per_call[-k:]) -
+                                           statistics.median(per_call[:k])) / am, 2),
+            "slowest_chunk": r["first_chunk"] + max(range(len(steps_ms)),
+                                                   key=lambda i: steps_ms[i]),
+        }
+    if "copy_calib" in r:
+        out["copy_calib"] = r["copy_calib"]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.dist)
     print(json.dumps(out), flush=True)

@@ -15,9 +15,9 @@ constexpr int kMaxSegments = KVC_MAX_WINDOW + 3;   // cond + sink + W + current
 constexpr int kTileKeys = KVC_TILE_KEYS;
 
 // Attention work decomposition (shared by the launcher and the workspace
-// sizing): a row is kAttnRowQueries queries of one head, run by kAttnWaves
-// waves; at most kAttnMaxWg persistent workgroups split the rows' key tiles.
-constexpr int kAttnWaves = 2;
+// sizing): a row is kAttnRowQueries queries of one head, run by one
+// workgroup; at most kAttnMaxWg persistent workgroups split the rows' key
+// tiles.
 constexpr int kAttnRowQueries = 128;
 constexpr int kAttnMaxWg = 512;
 

@@ -1,0 +1,144 @@
+"""Summaries of rocprofv3 CSV output for the profiles/ folder.
+
+    python -m chunked_attention_amd.profiling stats DIR --cmd "..." --out FILE.md
+        kernel statistics (--kernel-trace --stats --output-format csv run in DIR)
+    python -m chunked_attention_amd.profiling traffic --fetch DIR --write DIR \\
+        --calib-mib M --cmd-fetch "..." --cmd-write "..." --out FILE.json --md FILE.md
+        HBM bytes per launch of the attention kernel from two counter runs
+        (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch), each scaled by
+        the same counter's reading for a plain elementwise kernel that reads
+        and writes M MiB once.
+
+Only the last `--steady` dispatches of the attention kernel are used: the
+earlier ones run while the window fills and attend fewer keys.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCE = os.path.join(ROOT, "chunked_attention_amd", "csrc", "attn_fwd.hip")
+ATTN = "attn_fwd_bf16"
+CALIB = "neg_kernel"
+
+
+def _one(dirname: str, pattern: str) -> str:
+    hits = sorted(glob.glob(os.path.join(dirname, "**", pattern), recursive=True))
+    if not hits:
+        raise SystemExit(f"no {pattern} under {dirname}")
+    return hits[-1]
+
+
+def short_name(name: str) -> str:
+    for key in (ATTN, "cache_write", "cache_amax", "cache_quant", "fill_u32", CALIB):
+        if key in name:
+            if key == ATTN:
+                i = name.find("ILi")
+                return ATTN + (name[i:name.find("EEEv")] if i >= 0 else "")
+            return key
+    return name[:60]
+
+
+def stats_md(dirname: str, cmd: str) -> str:
+    path = _one(dirname, "*kernel_stats.csv")
+    rows = list(csv.DictReader(open(path)))
+    out = ["# rocprofv3 kernel statistics", "", "Command (from the repository root):", "",
+           "```", cmd, "```", "",
+           "| kernel | calls | total us | average us | min us | max us | % time |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        ns = lambda k: float(r[k]) / 1e3
+        out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {ns('TotalDurationNs'):.1f} | "
+                   f"{ns('AverageNs'):.2f} | {ns('MinNs'):.2f} | {ns('MaxNs'):.2f} | "
+                   f"{float(r['Percentage']):.2f} |")
+    out.append("")
+    return "\n".join(out)
+
+
+def _counter(dirname: str, counter: str):
+    path = _one(dirname, "*counter_collection.csv")
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        did = int(r["Dispatch_Id"])
+        per.setdefault(did, [r["Kernel_Name"], 0.0])
+        per[did][1] += float(r["Counter_Value"])
+    return [per[d] for d in sorted(per)]
+
+
+def traffic(fetch_dir, write_dir, calib_mib, steady):
+    calib_bytes = calib_mib << 20
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter(d, counter)
+        attn = [v for n, v in rows if ATTN in n][-steady:]
+        cal = [v for n, v in rows if CALIB in n]
+        if not attn or not cal:
+            raise SystemExit(f"{counter}: no attention or calibration dispatches in {d}")
+        kib_attn = statistics.mean(attn)
+        kib_cal = statistics.median(cal)
+        factor = calib_bytes / (kib_cal * 1024.0)
+        res[counter] = {"attn_kib_per_dispatch": kib_attn, "attn_dispatches": len(attn),
+                        "calib_kib_per_dispatch": kib_cal, "calib_bytes": calib_bytes,
+                        "scale": factor, "attn_bytes": kib_attn * 1024.0 * factor}
+    total = res["FETCH_SIZE"]["attn_bytes"] + res["WRITE_SIZE"]["attn_bytes"]
+    return res, total
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("dir")
+    a.add_argument("--cmd", required=True)
+    a.add_argument("--out", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("--fetch", required=True)
+    b.add_argument("--write", required=True)
+    b.add_argument("--calib-mib", type=int, required=True)
+    b.add_argument("--steady", type=int, default=3)
+    b.add_argument("--cmd-fetch", required=True)
+    b.add_argument("--cmd-write", required=True)
+    b.add_argument("--workload", default="720p steady chunk (8356 keys)")
+    b.add_argument("--out", required=True)
+    b.add_argument("--md", required=True)
+    args = ap.parse_args(argv)
+    if args.what == "stats":
+        open(args.out, "w").write(stats_md(args.dir, args.cmd))
+        return 0
+    res, total = traffic(args.fetch, args.write, args.calib_mib, args.steady)
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    rec = {"kernel": ATTN, "workload": args.workload, "kernel_source_sha256": sha,
+           "hbm_bytes_per_launch": round(total), "counters": res,
+           "commands": {"FETCH_SIZE": args.cmd_fetch, "WRITE_SIZE": args.cmd_write}}
+    json.dump(rec, open(args.out, "w"), indent=1)
+    f, wr = res["FETCH_SIZE"], res["WRITE_SIZE"]
+    md = ["# HBM traffic of the attention kernel (rocprofv3 counters)", "",
+          f"Workload: {args.workload}.  Counters in KiB per dispatch, averaged over the "
+          f"last {f['attn_dispatches']} attention dispatches (steady state); each counter "
+          f"is scaled by bytes / reading of a plain elementwise kernel that reads and writes "
+          f"{args.calib_mib} MiB once.", "",
+          "Commands (from the repository root):", "", "```", args.cmd_fetch, args.cmd_write,
+          "```", "",
+          "| counter | attention KiB/dispatch | calibration KiB/dispatch | scale | bytes/launch |",
+          "|---|---|---|---|---|",
+          f"| FETCH_SIZE | {f['attn_kib_per_dispatch']:.0f} | {f['calib_kib_per_dispatch']:.0f} | "
+          f"{f['scale']:.4f} | {f['attn_bytes'] / 1e6:.1f} MB |",
+          f"| WRITE_SIZE | {wr['attn_kib_per_dispatch']:.0f} | {wr['calib_kib_per_dispatch']:.0f} | "
+          f"{wr['scale']:.4f} | {wr['attn_bytes'] / 1e6:.1f} MB |",
+          "", f"Total HBM bytes per launch: {total / 1e6:.1f} MB.  Kernel source sha256 "
+          f"{sha[:16]}...", ""]
+    open(args.md, "w").write("\n".join(md))
+    print(json.dumps({"hbm_bytes_per_launch": round(total)}))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())

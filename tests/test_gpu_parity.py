@@ -147,6 +147,51 @@ def test_segment_offset_stress(where, shift):
         r.evict()
 
 
+@pytest.mark.parametrize("where", ["cond", "current"])
+@pytest.mark.parametrize("shift", [100.0, -100.0, 200.0])
+def test_offset_on_some_queries(where, shift):
+    # Only queries 40..49 and 150..170 see the offset: they fall in different
+    # waves and query rows, so only part of a workgroup needs the kernel's
+    # second pass.  A shift of 100 (144 in log2 units) overflows the fp32 row
+    # sum of the first pass when the large logits come after the first keys,
+    # which makes the kernel find the true max before recomputing.
+    w = synth.Workload("stress2", 4, 128, 200, 70, 2, 4, seed=23)
+    s = synth.Stream(w, "sharp")
+    sel = torch.zeros(w.chunk_tokens, dtype=torch.bool)
+    sel[40:50] = True
+    sel[150:171] = True
+    r = ring_for(w)
+    ck, cv = s.kv_cond()
+    ckr = synth.zero_feature0(ck)
+    if where == "cond":
+        _, ckr = synth.offset_segment(s.q(0), ck, shift, w.scale)
+    r.cond(ckr.cuda(), cv.cuda())
+    so = O1.StreamOracle(w.window, w.scale, O1.as_f64(ckr), O1.as_f64(cv))
+    for t in range(w.chunks):
+        k, v = s.kv_noisy(t)
+        q = s.q(t).clone()
+        q[..., 0] = 0.0
+        q[sel, :, 0] = 1.0
+        if where == "current":
+            _, k = synth.offset_segment(q, k, shift, w.scale)
+        else:
+            k = synth.zero_feature0(k)
+        r.stage(k.cuda(), v.cuda())
+        lse = torch.empty(w.heads, w.chunk_tokens, dtype=torch.float32, device="cuda")
+        o = r.attention(q.cuda(), lse=lse)
+        o2 = r.attention(q.cuda())
+        ref, ref_lse = so.attend(t, O1.as_f64(q), O1.as_f64(k), O1.as_f64(v))
+        assert_bf16_parity(compare(o, ref), f"some-queries {where} {shift} t={t}")
+        assert_bf16_parity(compare(o2, ref), f"some-queries {where} {shift} t={t} no lse")
+        err = np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse).max()
+        assert err < 2e-3 * max(1.0, np.abs(ref_lse).max() / 100), err
+        kc, vc = s.kv_clean(t)
+        kc = synth.zero_feature0(kc)
+        r.commit(kc.cuda(), vc.cuda())
+        so.commit(t, O1.as_f64(kc), O1.as_f64(vc))
+        r.evict()
+
+
 def test_long_stream_sampled_chunks():
     # W = 6 stream, 225 chunks from a pool of 4 input sets; parity on sampled
     # chunks (3 heads), including the first window-full chunk and the last.
