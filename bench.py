@@ -109,9 +109,10 @@ class Inputs:
 
 def run_stream_bench(w, args, device, flat: bool):
     """Streams chunks through `w.layers` rings.  The window is filled first
-    (untimed); then `warmup` untimed and `steps` timed steady-state chunks,
-    or, with `flat`, every chunk from the first full window to the end of
-    the stream, timed one by one."""
+    (untimed); then `warmup` untimed and `steps` timed steady-state chunks.
+    With `flat`, `warmup` chunks are streamed through a throwaway set of
+    rings first, then a fresh stream runs from chunk 0 to the end with every
+    chunk timed one by one."""
     import gc
     import torch
     import chunked_attention_amd as kv
@@ -119,16 +120,20 @@ def run_stream_bench(w, args, device, flat: bool):
 
     pool = min(args.pool, w.chunks) if args.pool else w.chunks
     inp = Inputs(w, pool, args.dist, device)
-    rings = [kv.Ring(w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window,
-                     kv_dtype=w.kv_dtype, device=device) for _ in range(w.layers)]
+    def new_rings():
+        rs = [kv.Ring(w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window,
+                      kv_dtype=w.kv_dtype, device=device) for _ in range(w.layers)]
+        if inp.cond:
+            for r in rs:
+                r.cond(*inp.cond)
+        return rs
+
+    rings = new_rings()
     outs = [torch.empty_like(inp.q[0][0]) for _ in range(2)]
-    if inp.cond:
-        for r in rings:
-            r.cond(*inp.cond)
     stream = torch.cuda.current_stream()
 
     if flat:
-        warmup, steps = 0, w.chunks - (w.window + 1)
+        warmup, steps = args.warmup, w.chunks
     else:
         warmup, steps = args.warmup, args.steps
     per_step = w.steps * w.layers * 3 + w.layers * 2 + 1
@@ -167,19 +172,29 @@ def run_stream_bench(w, args, device, flat: bool):
                 r.commit(*inp.clean[c])
             r.evict()
 
-    # fill the window (untimed) so every timed step is a steady-state chunk
     t = 0
-    while t <= w.window:
-        chunk(t, False)
-        t += 1
-    for _ in range(warmup):
-        chunk(t, False)
-        t += 1
+    if flat:
+        # warm the GPU up on a throwaway stream, then start over from chunk 0
+        for _ in range(warmup):
+            chunk(t, False)
+            t += 1
+        torch.cuda.synchronize()
+        rings = new_rings()
+        t = 0
+    else:
+        # fill the window (untimed) so every timed step is a steady-state chunk
+        while t <= w.window:
+            chunk(t, False)
+            t += 1
+        for _ in range(warmup):
+            chunk(t, False)
+            t += 1
     torch.cuda.synchronize()
     t_first = t
     start, end = next(ev_iter), next(ev_iter)
     # the timed region is host-driven: keep Python's collector from pausing
     # the launches (the GPU would idle behind it)
+    tele_before = gpu_telemetry() if flat else None
     gc.collect()
     gc.disable()
     try:
@@ -191,6 +206,7 @@ def run_stream_bench(w, args, device, flat: bool):
         torch.cuda.synchronize()
     finally:
         gc.enable()
+    tele_after = gpu_telemetry() if flat else None
     total_ms = start.elapsed_time(end)
     step_ms = [step_events[i].elapsed_time(step_events[i + 1])
                for i in range(len(step_events) - 1)] + [step_events[-1].elapsed_time(end)]
@@ -201,11 +217,13 @@ def run_stream_bench(w, args, device, flat: bool):
         "attn_ms": [a.elapsed_time(b) for a, b in attn_events],
         "write_ms": [a.elapsed_time(b) for a, b in write_events],
         "step_ms": step_ms,
-        "kv_len": kv_length(t_first, w.cond_tokens, w.chunk_tokens, w.window),
+        "kv_len": kv_length(max(t_first, w.window + 1), w.cond_tokens, w.chunk_tokens,
+                            w.window),
         "first_chunk": t_first,
         "last_chunk": t - 1,
         "calls_per_step": w.steps * w.layers,
         "writes_per_step": (w.steps + 1) * w.layers,
+        "telemetry": {"before": tele_before, "after": tele_after} if flat else None,
     }
     if args.copy_calib_mib:
         # a plain device copy of known size, for scaling the HBM byte counters
@@ -223,6 +241,48 @@ def run_stream_bench(w, args, device, flat: bool):
         res["copy_calib"] = {"bytes_each_way": nbytes,
                              "gbps": 2 * nbytes * 3 / (c0.elapsed_time(c1) * 1e-3) / 1e9}
     return res
+
+
+def _rolling_median_dev(xs, m, k=5):
+    meds = [statistics.median(xs[i:i + k]) for i in range(0, len(xs) - k + 1)]
+    return round(100 * max(abs(x - m) for x in meds) / m, 2) if meds else None
+
+
+def flatness(step_ms, attn_ms, window):
+    """Per-chunk time series of a whole stream (chunk i at index i): deviation
+    from the steady median over the window-full chunks [W+1, T-1] as a
+    5-chunk rolling median and raw, and literally from chunk 4 on."""
+    out = {"chunks_timed": len(step_ms)}
+    for name, lo in (("window_full", window + 1), ("from_chunk_4", 4)):
+        if lo >= len(step_ms):
+            continue
+        st, at = step_ms[lo:], attn_ms[lo:]
+        sm, am = statistics.median(st), statistics.median(at)
+        out[name] = {
+            "chunks": [lo, len(step_ms) - 1],
+            "step_ms_median": round(sm, 4),
+            "step_rolling5_max_dev_pct": _rolling_median_dev(st, sm),
+            "step_raw_max_dev_pct": round(100 * max(abs(x - sm) for x in st) / sm, 2),
+            "attn_us_median": round(am * 1e3, 2),
+            "attn_rolling5_max_dev_pct": _rolling_median_dev(at, am),
+            "attn_raw_max_dev_pct": round(100 * max(abs(x - am) for x in at) / am, 2),
+        }
+    out["step_ms_series"] = [round(x, 4) for x in step_ms]
+    return out
+
+
+def gpu_telemetry():
+    """Shader clock and temperature as rocm-smi reports them (best effort)."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocm-smi", "--showtemp", "--showclocks", "--json"],
+                             capture_output=True, text=True, timeout=20).stdout
+        data = json.loads(txt)
+    except Exception:  # noqa: BLE001 - telemetry is optional
+        return None
+    card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
+    return {k: v for k, v in card.items()
+            if "sclk" in k.lower() or "temperature" in k.lower()}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_720p_traffic.json")
@@ -254,6 +314,8 @@ def main() -> int:
     ap.add_argument("--pool", type=int, default=16, help="distinct input chunks uploaded")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--window", type=int, default=None,
+                    help="override the config's window W (e.g. the long stream at W=3)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -276,10 +338,18 @@ def main() -> int:
         args.pool = min(args.pool, 4)
         args.steps = min(args.steps, 20)
         args.warmup = min(args.warmup, 2)
+    if args.window is not None:
+        import dataclasses
+        w = dataclasses.replace(w, window=args.window, name=f"{w.name}-W{args.window}")
     flat = args.config == "long"
 
     r = run_stream_bench(w, args, device, flat)
     flops = attn_flops(w, r["kv_len"])
+    if flat:
+        # throughput over the window-full chunks only
+        steady = slice(w.window + 1, None)
+        r["ms_per_step"] = statistics.mean(r["step_ms"][steady])
+        r["attn_ms_all"], r["attn_ms"] = r["attn_ms"], r["attn_ms"][steady]
     step_s = r["ms_per_step"] / 1e3
     attn_us = statistics.mean(r["attn_ms"]) * 1e3
     attn_med_us = statistics.median(r["attn_ms"]) * 1e3
@@ -340,26 +410,8 @@ def main() -> int:
         },
     }
     if flat:
-        per_call = r["attn_ms"]
-        am = statistics.median(per_call)
-        k = max(1, len(steps_ms) // 10)
-        q95 = lambda xs, m: round(100 * sorted(abs(x - m) for x in xs)[int(0.95 * (len(xs) - 1))]
-                                  / m, 2)
-        out["flatness"] = {
-            "chunks": [r["first_chunk"], r["last_chunk"]],
-            "step_ms_median": round(med, 4),
-            "step_ms_max_dev_pct": dev(steps_ms, med),
-            "step_ms_p95_dev_pct": q95(steps_ms, med),
-            "step_ms_drift_pct": round(100 * (statistics.median(steps_ms[-k:]) -
-                                              statistics.median(steps_ms[:k])) / med, 2),
-            "attn_us_median": round(am * 1e3, 2),
-            "attn_max_dev_pct": dev(per_call, am),
-            "attn_p95_dev_pct": q95(per_call, am),
-            "attn_drift_pct": round(100 * (statistics.median(per_call[-k:]) -
-                                           statistics.median(per_call[:k])) / am, 2),
-            "slowest_chunk": r["first_chunk"] + max(range(len(steps_ms)),
-                                                   key=lambda i: steps_ms[i]),
-        }
+        out["flatness"] = flatness(r["step_ms"], r["attn_ms_all"], w.window)
+        out["flatness"]["telemetry"] = r.get("telemetry")
     if "copy_calib" in r:
         out["copy_calib"] = r["copy_calib"]
     if not args.no_cpu_baseline:
