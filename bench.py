@@ -405,7 +405,7 @@ def main() -> int:
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel": f"attn_fwd_bf16<{w.head_dim},1,false>" if not fp8 else
-                      f"attn_fwd_fp8<{w.head_dim}>",
+                      f"attn_fwd_fp8<{w.head_dim},false>",
             "per_launch_flops": flops,
         },
     }

@@ -1,0 +1,335 @@
+// Pieces shared by the bf16 (attn_fwd.hip) and fp8 (attn_fwd_fp8.hip)
+// attention kernels: kernel arguments, the persistent stream-K work split,
+// tile cursors over the ring's segments, LDS copies, waits and barriers, and
+// the end of a row piece (normalise and store, or hand a partial result to
+// the piece that merges the row).
+//
+// Work: a "row" is 128 queries of one head; its keys are T tiles of 64 keys
+// over all visible segments.  A workgroup of 4 waves (32 queries each) runs
+// one row piece at a time; nwg persistent workgroups split the R*T (row,
+// tile) steps into equal contiguous ranges.  A row cut between workgroups is
+// finished by the last piece to arrive, which merges every piece's partial
+// (O, reference, sums) in piece order, so results do not depend on timing.
+#pragma once
+
+#include <algorithm>
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "kvc_internal.hpp"
+
+namespace kvc {
+namespace attn {
+
+constexpr int kBq = kAttnRowQueries;    // queries per row (128)
+constexpr int kBk = kTileKeys;          // keys per tile (64)
+constexpr int kWaves = 4;               // waves per workgroup, 32 queries each
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQW = 32;                 // queries per wave
+constexpr int kMaxWg = kAttnMaxWg;      // persistent workgroups at most (2 per CU)
+constexpr int kMinPieceTiles = 16;      // smallest share of a row worth splitting off
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMl = 3 * 32;             // per wave: (reference, sum, exact sum) per query
+static_assert(kWaves * kQW == kBq, "row = waves x queries per wave");
+
+struct SegArg {
+  const unsigned char* k;   // [H][pitch][d]
+  const unsigned char* vt;  // [H][d][pitch]
+  const float* ks;          // [H] K scales (fp8 rings)
+  const float* vs;          // [H] V scales (fp8 rings)
+  int rows;
+  int pitch;
+  int tile0;                // first tile of this segment in the row's tile list
+  int pad_;
+};
+
+struct AttnArgs {
+  const uint16_t* q;
+  uint16_t* o;
+  float* lse;
+  float* part_o;            // [2*nwg][kBq*D] partial O, accumulator layout
+  float* part_ml;           // [2*nwg][waves][3][32] partial reference, sum, exact sum
+  unsigned* counters;       // [nrows][2]: arrived, partials written
+  int n;
+  int heads;
+  float c;                  // softmax scale * log2(e)
+  int nseg;
+  int ntiles;               // tiles per row (T)
+  int nqt;                  // rows per head
+  int nrows;                // heads * nqt
+  int nwg;                  // persistent workgroups
+  long long total;          // nrows * ntiles
+  SegArg seg[kMaxSegments];
+};
+
+// max / sum of a value with the one held by lane ^ 32 (v_permlane32_swap
+// exchanges the two 32-lane halves)
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// first step of workgroup w's range, and the owner of step x
+__device__ __forceinline__ long long range_begin(long long w, const AttnArgs& a) {
+  return w * a.total / a.nwg;
+}
+__device__ __forceinline__ int owner_of(long long x, const AttnArgs& a) {
+  return static_cast<int>(((x + 1) * a.nwg - 1) / a.total);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// buffer resource over `bytes` bytes at `base` (raw buffer: stride 0, offsets
+// in bytes; 0x00020000 = 32-bit data format, the gfx9 setting for raw access)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// 16 bytes per lane from the buffer at voff + soff into LDS at lds + 16*lane
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, static_cast<int>(voff),
+                                           static_cast<int>(soff), 0, 0);
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt low bits [3:0], high
+// bits [15:14]; expcnt [6:4], left at its maximum; lgkmcnt [11:8])
+template <int N>
+__device__ __forceinline__ void wait_vm_keep_lds_done() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+}
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// Workgroup barrier without a memory fence (a fence would make the compiler
+// wait for every copy in flight).  Written as an asm statement with a memory
+// clobber so that no memory access is moved across it at any compiler level;
+// it emits no wait of its own.  The caller has already waited for its own LDS
+// accesses and for the copies the next step reads.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Cursor over one row's key tiles: segment, first key of the tile, and that
+// segment's fields, all wave-uniform (scalar registers).  Moving to the next
+// tile touches no memory except when a segment ends.  E = bytes per stored
+// element.
+struct TileCursor {
+  int t;                    // tile index within the row
+  int s;                    // segment
+  int k0;                   // first key of the tile within the segment
+  int rows;
+  int pitch;
+  __amdgpu_buffer_rsrc_t rk;   // this head's K plane of the segment
+  __amdgpu_buffer_rsrc_t rv;   // this head's Vt plane
+};
+
+template <int D, int E>
+__device__ __forceinline__ void cursor_fields(const AttnArgs& a, TileCursor& c, int h) {
+  const SegArg& s = a.seg[c.s];
+  c.rows = s.rows;
+  c.pitch = s.pitch;
+  const uint32_t plane = static_cast<uint32_t>(s.pitch) * D * E;
+  c.rk = make_rsrc(s.k + static_cast<size_t>(h) * plane, plane);
+  c.rv = make_rsrc(s.vt + static_cast<size_t>(h) * plane, plane);
+}
+template <int D, int E>
+__device__ __forceinline__ void cursor_seek(const AttnArgs& a, TileCursor& c, int t, int h) {
+  int s = 0;
+  while (s + 1 < a.nseg && a.seg[s + 1].tile0 <= t) ++s;
+  c.t = t;
+  c.s = s;
+  c.k0 = (t - a.seg[s].tile0) * kBk;
+  cursor_fields<D, E>(a, c, h);
+}
+// one tile on, but never past tile `last`
+template <int D, int E>
+__device__ __forceinline__ void cursor_next(const AttnArgs& a, TileCursor& c, int last, int h) {
+  if (c.t >= last) return;
+  ++c.t;
+  c.k0 += kBk;
+  if (c.k0 >= c.rows) {
+    ++c.s;
+    c.k0 = 0;
+    cursor_fields<D, E>(a, c, h);
+  }
+}
+
+// workgroup-wide OR of two per-wave flags (every wave must take the same path
+// when the paths contain barriers)
+__device__ __forceinline__ void vote2(int (&slot)[kWaves][2], int wave, int lane, bool p0,
+                                      bool p1, bool& any0, bool& any1) {
+  const bool w0 = __any(p0), w1 = __any(p1);
+  if (lane == 0) {
+    slot[wave][0] = w0;
+    slot[wave][1] = w1;
+  }
+  __syncthreads();
+  any0 = any1 = false;
+#pragma unroll
+  for (int v = 0; v < kWaves; ++v) {
+    any0 = any0 || slot[v][0];
+    any1 = any1 || slot[v][1];
+  }
+}
+
+// End of a row piece.  oacc holds this wave's unnormalised O^T (accumulator
+// layout: register i of block db is feature db*32 + (i/4)*8 + (lane/32)*4 +
+// i%4 of query qbase + lane%32), m_run the reference (log2 units), l_tot the
+// row sum that normalises O, le_tot the sum for the lse output.  A piece that
+// covers its whole row writes O / l (bf16) and lse; otherwise it stores its
+// partial, and the last piece of the row to arrive merges all partials in
+// piece order.  `s_ticket` is a workgroup-shared word.
+template <int D, bool kLse>
+__device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)[D / 32],
+                                             float m_run, float l_tot, float le_tot, int r,
+                                             int h, int qbase, bool first_piece, int w,
+                                             int wave, int lane, unsigned& s_ticket) {
+  constexpr int kDB = D / 32;
+  const int tid = threadIdx.x;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const long long rs = static_cast<long long>(r) * a.ntiles;
+  const int w_lo = owner_of(rs, a);
+  const int w_hi = owner_of(rs + a.ntiles - 1, a);
+  if (w_hi > w_lo) {
+    // this row is split: the last piece to arrive merges the others
+    unsigned* arrived = a.counters + 2 * r;
+    unsigned* written = arrived + 1;
+    const unsigned npieces = static_cast<unsigned>(w_hi - w_lo + 1);
+    __syncthreads();
+    if (tid == 0)
+      s_ticket = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const bool last = s_ticket == npieces - 1;
+    const int slot = first_piece ? 0 : 1;
+    const size_t o_wave = static_cast<size_t>(wave) * kQW * D;
+    const size_t ml_wave = static_cast<size_t>(wave) * kMl;
+    if (!last) {
+      // Partials are written and read with device-scope relaxed atomics
+      // (write-through, coherent across the XCDs' L2s), ordered by waiting
+      // for completion before the counter update: no cache writeback needed.
+      float* po = a.part_o + static_cast<size_t>(2 * w + slot) * kBq * D + o_wave;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          __hip_atomic_store(po + (db * 16 + i) * 64 + lane, oacc[db][i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      float* pml = a.part_ml + static_cast<size_t>(2 * w + slot) * kWaves * kMl + ml_wave;
+      if (half == 0) {
+        __hip_atomic_store(pml + 0 * 32 + col, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pml + 1 * 32 + col, l_tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pml + 2 * 32 + col, le_tot, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): stores complete
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(written, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    // wait until every other piece has stored its partial (they have all
+    // arrived already, so this is a short wait), then merge in piece order
+    // whoever merges, so the result is bitwise the same from run to run:
+    // sum_i O_i 2^(m_i - m_max), starting from the first piece
+    if (tid == 0) {
+      for (int spin = 0; spin < (1 << 26); ++spin) {
+        if (__hip_atomic_load(written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+            npieces - 1)
+          break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __syncthreads();
+    float mmax = m_run;
+    for (int ow = w_lo; ow <= w_hi; ++ow) {
+      if (ow == w) continue;
+      const int oslot = range_begin(ow, a) >= rs ? 0 : 1;
+      const float* pml = a.part_ml + static_cast<size_t>(2 * ow + oslot) * kWaves * kMl + ml_wave;
+      mmax = fmaxf(mmax, __hip_atomic_load(pml + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    }
+    f32x16_t acc[kDB];
+    float l_acc = 0.f, le_acc = 0.f;
+    for (int ow = w_lo; ow <= w_hi; ++ow) {
+      const bool first = ow == w_lo;
+      float mo = m_run, lo = l_tot, leo = le_tot;
+      f32x16_t v[kDB];
+      if (ow == w) {
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) v[db] = oacc[db];
+      } else {
+        const int oslot = range_begin(ow, a) >= rs ? 0 : 1;
+        const float* po = a.part_o + static_cast<size_t>(2 * ow + oslot) * kBq * D + o_wave;
+        const float* pml =
+            a.part_ml + static_cast<size_t>(2 * ow + oslot) * kWaves * kMl + ml_wave;
+        mo = __hip_atomic_load(pml + 0 * 32 + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lo = __hip_atomic_load(pml + 1 * 32 + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        leo = __hip_atomic_load(pml + 2 * 32 + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            v[db][i] = __hip_atomic_load(po + (db * 16 + i) * 64 + lane, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      }
+      const float f = __builtin_amdgcn_exp2f(mo - mmax);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] = first ? v[db][i] * f : fmaf(v[db][i], f, acc[db][i]);
+      l_acc = first ? lo * f : fmaf(lo, f, l_acc);
+      le_acc = first ? leo * f : fmaf(leo, f, le_acc);
+    }
+#pragma unroll
+    for (int db = 0; db < kDB; ++db) oacc[db] = acc[db];
+    m_run = mmax;
+    l_tot = l_acc;
+    le_tot = le_acc;
+    if (tid == 0) {
+      __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(written, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  const int qi = qbase + col;
+  if (qi >= a.n) return;
+  const float inv = 1.0f / l_tot;
+  uint16_t* orow = a.o + (static_cast<size_t>(qi) * a.heads + h) * D;
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t wv[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const __bf16 lo = static_cast<__bf16>(oacc[db][g * 4 + 2 * e] * inv);
+        const __bf16 hi = static_cast<__bf16>(oacc[db][g * 4 + 2 * e + 1] * inv);
+        wv[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
+      }
+      *reinterpret_cast<uint2*>(orow + db * 32 + g * 8 + half * 4) = make_uint2(wv[0], wv[1]);
+    }
+  if (kLse && half == 0)
+    a.lse[static_cast<size_t>(h) * a.n + qi] = (m_run + __log2f(le_tot)) * kLn2;
+}
+
+// Host side: kernel arguments from a launch description (segment table,
+// tiles, rows, grid, workspace).  Returns KVC_OK or KVC_E_INVAL.
+kvc_status fill_args(const AttnDesc& d, AttnArgs& a);
+// zero `n` words on the stream (a kernel, not a memset: capturable)
+void launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t stream);
+
+// the fp8 launcher (attn_fwd_fp8.hip)
+kvc_status launch_fp8(const AttnDesc& d, hipStream_t stream);
+
+}  // namespace attn
+}  // namespace kvc

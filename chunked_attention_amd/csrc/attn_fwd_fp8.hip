@@ -1,0 +1,437 @@
+// K3: chunk-causal sink+window attention forward over an fp8 (E4M3) KV
+// cache, fp8 MFMA, gfx950.
+//
+// Same visible set, work split and pipeline as the bf16 kernel (see
+// attn_fwd.hip and attn_common.hpp); the KV cache holds E4M3 codes with one
+// float32 scale per (head, stored segment), so a segment's keys are
+// k = s_k * code and its values v = s_v * code.  Q stays bf16 in memory
+// (discuss.pytorch.kr "JoyAI-Video-Edit 소개", real-time deployment section:
+// the deployed pipeline runs with FP8 quantisation and a bounded KV cache).
+//
+// Per tile and wave (32 queries), with 32x32x64 fp8 MFMAs
+// (v_mfma_f32_32x32x64_f8f6f4, E4M3 x E4M3, fp32 accumulate):
+//   S^T[32 keys x 32 q] = K_half . Q8^T      (2 D/64 MFMAs per half tile)
+//   O^T[d x 32 q]      += Vt_tile . P8^T     (D/32 MFMAs per 64-key tile)
+//   l[32 q]            += 1 . P8^T           (one MFMA: an all-ones A operand
+//                                            gives every row the column sums)
+// The MFMA pairs byte j of A lane (row r, half h) with byte j of B lane
+// (column c, half h) over k = 64.
+// - Q is quantised per query when a row piece starts, in two parts:
+//   y = q * 448 / amax|q|, Q8hi = E4M3(y), Q8lo = E4M3(16 (y - Q8hi)); the
+//   scores take K . Q8hi + (K . Q8lo) / 16, the second product on the MFMA's
+//   block-scaled form (B scale 2^-4), so Q keeps about 8 significant bits.
+//   The logit is s = acc * s_q * s_k and the softmax multiplier is
+//   scale * log2(e) * s_q * s_k per segment.
+// - P is quantised to E4M3 and the row sum is taken over those same codes
+//   (by the ones MFMA), so O is an exact convex combination of the weights
+//   applied.  E4M3 saturates at 448: the piece's reference m_ref (max of its
+//   first 32 keys) must stay within 8 (log2 units) of every logit; the max
+//   is tracked and a piece that exceeds it is computed again with its true
+//   max as reference (then p <= 1).
+// - O accumulates in units of the current segment's V scale; when the tiles
+//   move to a segment with another scale, O is multiplied by s_old / s_new
+//   (at most once per segment, W+3 times per row), and by the last scale at
+//   the end.
+// Layout of the fp8 tiles in LDS: K rows of D bytes and Vt rows of 64 bytes,
+// 16-byte chunks XOR-swizzled so that 8 consecutive lanes' 16-byte reads hit
+// distinct bank groups: for 128-byte rows chunk c of row r lives at
+// c ^ (r & 7), for 64-byte rows at c ^ ((r >> 1) & 3).  The ring stores the
+// Vt columns of every 64-key tile in the order pi: column p holds key
+// ((p & 0x1C) << 1) | ((p & 0x20) >> 3) | (p & 3), which is the key a
+// lane's accumulator register delivers to B-operand byte p % 32 of lane half
+// p / 32.
+#include "attn_common.hpp"
+
+namespace kvc {
+namespace attn {
+namespace {
+
+constexpr float kP8Margin = 8.0f;   // largest p allowed before recomputing: 2^8
+constexpr int kMaxPasses = 3;
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int D>
+struct Geo8 {
+  static constexpr int kKRow = D;                   // bytes per K row
+  static constexpr int kKBytes = kBk * kKRow;       // K tile bytes
+  static constexpr int kVBytes = D * kBk;           // Vt tile bytes (D rows of 64 B)
+  static constexpr int kKInstr = kKBytes / 1024 / kWaves;
+  static constexpr int kVInstr = kVBytes / 1024 / kWaves;
+  static constexpr int kKS = D / 64;                // MFMA k-steps over d for QK^T
+  static constexpr int kDB = D / 32;                // 32-row blocks of O^T
+  static_assert(kKInstr >= 1 && kVInstr >= 1, "whole 1 KB copies per wave");
+};
+
+// byte offset of logical 16-byte chunk c of row r in a swizzled LDS tile
+// with rows of RB bytes
+template <int RB>
+__device__ __forceinline__ uint32_t swz(int r, int c) {
+  static_assert(RB == 128 || RB == 64, "row size");
+  if constexpr (RB == 128) return static_cast<uint32_t>(r * 128 + ((c ^ (r & 7)) * 16));
+  else return static_cast<uint32_t>(r * 64 + ((c ^ ((r >> 1) & 3)) * 16));
+}
+
+__device__ __forceinline__ i32x8_t ld32(const unsigned char* p0, const unsigned char* p1) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p0);
+  const uint4 b = *reinterpret_cast<const uint4*>(p1);
+  i32x8_t v;
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  return v;
+}
+
+__device__ __forceinline__ f32x16_t mfma8(const i32x8_t& a, const i32x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// the same product with B scaled by 2^-4 (block scale E8M0 123; A scale 127 = 1)
+__device__ __forceinline__ f32x16_t mfma8_b16th(const i32x8_t& a, const i32x8_t& b,
+                                               const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 123);
+}
+
+// two floats to E4M3 codes (nearest, ties to even) in the low or high half
+template <bool kHigh>
+__device__ __forceinline__ int pack8(float x, float y, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(x, y, old, kHigh);
+}
+
+template <int D, bool kLse>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_fp8(const AttnArgs a) {
+  using G = Geo8<D>;
+  constexpr int kKS = G::kKS;
+  constexpr int kDB = G::kDB;
+  constexpr int kK0 = 0, kK1 = 1, kV0 = 2, kV1 = 3;
+  __shared__ __attribute__((aligned(1024))) unsigned char kb0[G::kKBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb1[G::kKBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb0[G::kVBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb1[G::kVBytes];
+  auto buf = [&](int b) -> unsigned char* {
+    return b == kK0 ? kb0 : b == kK1 ? kb1 : b == kV0 ? vb0 : vb1;
+  };
+  __shared__ unsigned s_ticket;
+  __shared__ int s_vote[kWaves][2];
+
+  const int w = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  // Per-lane byte offsets of the copies (16 bytes per lane, 1 KB per wave
+  // instruction).  K: a 1 KB block holds 1024 / D rows; lane l fills chunk
+  // l % (D/16) of row l / (D/16) and fetches the logical chunk that the
+  // swizzle puts there; the swizzle of a row depends on the lane only.  Vt:
+  // a 1 KB block holds 16 rows of 64 bytes.
+  constexpr int kKLanesPerRow = D / 16;
+  const int krow = lane / kKLanesPerRow;
+  const int kpc = lane % kKLanesPerRow;
+  const int klog = D == 128 ? (kpc ^ (krow & 7)) : (kpc ^ ((krow >> 1) & 3));
+  const uint32_t koff = static_cast<uint32_t>(krow * D + klog * 16);
+  const int vrow = lane >> 2;
+  const int vlog = (lane & 3) ^ ((vrow >> 1) & 3);
+
+  auto dma_k = [&](auto dst_tag, const TileCursor& c) {
+    constexpr int DST = decltype(dst_tag)::value;
+    const uint32_t sbase = static_cast<uint32_t>(c.k0) * G::kKRow;
+#pragma unroll
+    for (int u = 0; u < G::kKInstr; ++u) {
+      const int blk = wave * G::kKInstr + u;
+      dma16(c.rk, buf(DST) + blk * 1024, koff, sbase + blk * 1024);
+    }
+  };
+  auto dma_v = [&](auto dst_tag, const TileCursor& c) {
+    constexpr int DST = decltype(dst_tag)::value;
+    const uint32_t pitch = static_cast<uint32_t>(c.pitch);
+    const uint32_t voff = static_cast<uint32_t>(vrow) * pitch + vlog * 16;
+#pragma unroll
+    for (int u = 0; u < G::kVInstr; ++u) {
+      const int blk = wave * G::kVInstr + u;
+      dma16(c.rv, buf(DST) + blk * 1024, voff,
+            static_cast<uint32_t>(blk) * 16 * pitch + static_cast<uint32_t>(c.k0));
+    }
+  };
+
+  // K operands of one 32-key half tile (rows hh*32 + col): 32 bytes of
+  // features ks*64 + half*32 .. +31 per k-step
+  auto read_kops = [&](const unsigned char* kt, int hh, i32x8_t (&kops)[kKS]) {
+    const int r = hh * 32 + col;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+      kops[ks] = ld32(kt + swz<D>(r, ks * 4 + half * 2), kt + swz<D>(r, ks * 4 + half * 2 + 1));
+  };
+  // scores: K . (Q8hi + Q8lo / 16)^T
+  auto qk = [&](const i32x8_t (&kops)[kKS], const i32x8_t (&qhi)[kKS], const i32x8_t (&qlo)[kKS],
+                f32x16_t& s) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      s = mfma8(kops[ks], qhi[ks], s);
+      s = mfma8_b16th(kops[ks], qlo[ks], s);
+    }
+  };
+  auto mask = [&](f32x16_t& sc, int valid) {
+    if (valid < 32) {
+      const int lim = valid - half * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const bool keep = (i >> 2) * 8 + (i & 3) < lim;
+        sc[i] = keep ? sc[i] : -INFINITY;
+      }
+    }
+  };
+  auto raw_max = [&](const f32x16_t& sc) -> float {
+    float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+    return xor32_max(mx);
+  };
+
+  i32x8_t ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0 in every byte
+
+  for (long long x = range_begin(w, a), xe = range_begin(w + 1, a); x < xe;) {
+    const int r = static_cast<int>(x / a.ntiles);
+    const int t0 = static_cast<int>(x % a.ntiles);
+    const long long rest = xe - x;
+    const int t1 = rest < a.ntiles - t0 ? t0 + static_cast<int>(rest) : a.ntiles;
+    const bool first_piece = x == range_begin(w, a);
+    x += t1 - t0;
+    const int h = r / a.nqt;
+    const int qbase = (r - h * a.nqt) * kBq + wave * kQW;
+
+    // Q^T as B operands: lane holds query qbase + col, byte j of k-step ks
+    // = feature ks*64 + half*32 + j.  q / s_q = Q8hi + Q8lo / 16 (E4M3 of
+    // the value, then E4M3 of 16 x the remainder): about 8 significant bits,
+    // like bf16, for two fp8 MFMAs per k-step
+    i32x8_t q8[kKS], q8lo[kKS];
+    float cq;   // scale * log2(e) * s_q
+    {
+      const int qi = qbase + col;
+      float qv[kKS][32];
+      const uint16_t* qrow = a.q + (static_cast<size_t>(qi) * a.heads + h) * D + half * 32;
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          uint4 u = make_uint4(0, 0, 0, 0);
+          if (qi < a.n) u = ld16(qrow + ks * 64 + c4 * 8);
+          const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qv[ks][c4 * 8 + 2 * e] = bf16_bits_to_float(wv[e] & 0xFFFFu);
+            qv[ks][c4 * 8 + 2 * e + 1] = bf16_bits_to_float(wv[e] >> 16);
+          }
+        }
+      float amax = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(qv[ks][j]));
+      amax = xor32_max(amax);
+      const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+      cq = a.c * (amax > 0.f ? amax / 448.0f : 1.0f);
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = qv[ks][4 * v + e] * inv;
+          const int hi = pack8<true>(y[2], y[3], pack8<false>(y[0], y[1], 0));
+          const auto d01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+          const auto d23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+          q8[ks][v] = hi;
+          q8lo[ks][v] = pack8<true>((y[2] - d23[0]) * 16.0f, (y[3] - d23[1]) * 16.0f,
+                                    pack8<false>((y[0] - d01[0]) * 16.0f,
+                                                 (y[1] - d01[1]) * 16.0f, 0));
+        }
+    }
+
+    f32x16_t oacc[kDB];
+    f32x16_t lacc;
+    float m_ref = 0.f, m_seen = -INFINITY;
+    float vs_cur = 1.f;
+    const int tlast = t1 - 1;
+    for (int pass = 0;; ++pass) {
+      m_seen = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+      int pv_seg = -1;
+      f32x16_t sacc[2];
+      int pf[2][4];   // E4M3 P of the two half tiles: byte (i%4) of word i/4
+
+      TileCursor cj, cv, ck;
+      cursor_seek<D, 1>(a, cj, t0, h);
+      cv = cj;
+      cursor_next<D, 1>(a, cv, tlast, h);
+      ck = cv;
+      cursor_next<D, 1>(a, ck, tlast, h);
+      // softmax multiplier of the tile whose scores are being consumed
+      auto ceff = [&](const TileCursor& c) { return cq * a.seg[c.s].ks[h]; };
+
+      __syncthreads();
+      dma_k(std::integral_constant<int, kK0>{}, cj);
+      dma_v(std::integral_constant<int, kV0>{}, cj);
+      dma_k(std::integral_constant<int, kK1>{}, cv);
+      wait_dma();
+      __syncthreads();
+      {
+        i32x8_t kops[kKS];
+        read_kops(buf(kK0), 0, kops);
+        qk(kops, q8, q8lo, sacc[0]);
+      }
+      if (pass == 0) {
+        f32x16_t first = sacc[0];
+        mask(first, cj.rows - cj.k0);
+        m_ref = raw_max(first) * ceff(cj);
+      }
+
+      auto half_step = [&](auto u_tag) {
+        constexpr int U = decltype(u_tag)::value;
+        constexpr int HH = U & 1;
+        constexpr int TP = (U >> 1) & 1;
+        constexpr int CUR = U & 1;
+        constexpr int KJ = TP == 0 ? kK0 : kK1;
+        constexpr int KN = TP == 0 ? kK1 : kK0;
+        constexpr int VJ = TP == 0 ? kV0 : kV1;
+        constexpr int VN = TP == 0 ? kV1 : kV0;
+        if (HH == 0) {
+          dma_v(std::integral_constant<int, VN>{}, cv);   // V_{j+1}; V_{j-1} is done
+        } else {
+          dma_k(std::integral_constant<int, KJ>{}, ck);   // K_{j+2}; K_j is done
+        }
+        i32x8_t kops[kKS];
+        if (HH == 0) {
+          read_kops(buf(KJ), 1, kops);
+        } else {
+          read_kops(buf(KN), 0, kops);
+        }
+
+        f32x16_t& sc = sacc[CUR];
+        mask(sc, cj.rows - cj.k0 - HH * 32);
+        const float c_eff = ceff(cj);
+        m_seen = fmaxf(m_seen, raw_max(sc) * c_eff);
+
+        qk(kops, q8, q8lo, sacc[1 - CUR]);
+
+        const float neg_m = -m_ref;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[4 * v + 0], c_eff, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[4 * v + 1], c_eff, neg_m));
+          const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[4 * v + 2], c_eff, neg_m));
+          const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[4 * v + 3], c_eff, neg_m));
+          pf[HH][v] = pack8<true>(p2, p3, pack8<false>(p0, p1, 0));
+        }
+
+        if (HH == 1) {
+          // this tile's values: rescale O if the tile starts a segment with
+          // another V scale, then O^T += Vt . P^T and l += 1 . P^T
+          if (cj.s != pv_seg) {
+            const float vs_new = a.seg[cj.s].vs[h];
+            if (pv_seg >= 0) {
+              const float f = vs_cur / vs_new;
+#pragma unroll
+              for (int db = 0; db < kDB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[db][i] *= f;
+            }
+            vs_cur = vs_new;
+            pv_seg = cj.s;
+          }
+          i32x8_t pb;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            pb[v] = pf[0][v];
+            pb[4 + v] = pf[1][v];
+          }
+          const unsigned char* vt = buf(VJ);
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) {
+            const int rr = db * 32 + col;
+            const i32x8_t vops = ld32(vt + swz<64>(rr, half * 2), vt + swz<64>(rr, half * 2 + 1));
+            oacc[db] = mfma8(vops, pb, oacc[db]);
+          }
+          lacc = mfma8(ones, pb, lacc);
+        }
+        if (HH == 0) {
+          wait_vm_keep_lds_done<G::kVInstr>();
+        } else {
+          wait_vm_keep_lds_done<G::kKInstr>();
+        }
+        barrier_no_fence();
+        if (HH == 1) {
+          cursor_next<D, 1>(a, cj, tlast, h);
+          cursor_next<D, 1>(a, cv, tlast, h);
+          cursor_next<D, 1>(a, ck, tlast, h);
+        }
+      };
+
+      int j = t0;
+      for (; j + 1 < t1; j += 2) {
+        half_step(std::integral_constant<int, 0>{});
+        half_step(std::integral_constant<int, 1>{});
+        half_step(std::integral_constant<int, 2>{});
+        half_step(std::integral_constant<int, 3>{});
+      }
+      if (j < t1) {
+        half_step(std::integral_constant<int, 0>{});
+        half_step(std::integral_constant<int, 1>{});
+      }
+      wait_dma();
+      if (pass + 1 >= kMaxPasses) break;
+      // a logit more than 2^8 above the reference would saturate E4M3 P:
+      // recompute with the true max (NaN passes)
+      const bool over = m_seen > m_ref + kP8Margin;
+      bool any_over, unused;
+      vote2(s_vote, wave, lane, over, false, any_over, unused);
+      if (!any_over) break;
+      if (over) m_ref = m_seen;
+    }
+    // O in true units; the row sum is the same in every accumulator row
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[db][i] *= vs_cur;
+    const float l_tot = lacc[0];
+    finish_piece<D, kLse>(a, oacc, m_ref, l_tot, l_tot, r, h, qbase, first_piece, w, wave, lane,
+                          s_ticket);
+  }
+}
+
+template <int D>
+kvc_status launch_fp8_d(const AttnDesc& d, hipStream_t stream) {
+  AttnArgs a;
+  const kvc_status st = fill_args(d, a);
+  if (st != KVC_OK) return st;
+  for (int s = 0; s < a.nseg; ++s)
+    if (!a.seg[s].ks || !a.seg[s].vs) return KVC_E_INVAL;
+  if (!d.workspace_ready) launch_fill_u32(a.counters, 2 * a.nrows, 0u, stream);
+  if (a.lse)
+    hipLaunchKernelGGL((attn_fwd_fp8<D, true>), dim3(a.nwg), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_fp8<D, false>), dim3(a.nwg), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_DEVICE;
+}
+
+}  // namespace
+
+kvc_status launch_fp8(const AttnDesc& d, hipStream_t stream) {
+  switch (d.head_dim) {
+    case 64: return launch_fp8_d<64>(d, stream);
+    case 128: return launch_fp8_d<128>(d, stream);
+    default: return KVC_E_UNSUPPORTED;
+  }
+}
+
+}  // namespace attn
+}  // namespace kvc

@@ -2,10 +2,12 @@
 // layout [rows][H][d] into a ring slot: K head-major [H][pitch][d] and V
 // transposed per head [H][d][pitch] (the layout the attention kernel's PV
 // product reads), zero-filling the padded rows.  Within every group of 16
-// keys the V columns are stored in the order kappa (swap of key-index bits 2
-// and 3), which is the order in which the attention kernel's score
+// keys the bf16 V columns are stored in the order kappa (swap of key-index
+// bits 2 and 3), which is the order in which the attention kernel's score
 // accumulator hands keys to the PV product.  The fp8 variant quantises to
-// E4M3 with one float32 scale per (head, slot).
+// E4M3 with one float32 scale per (head, slot) and stores the V columns of
+// every 64-key tile in the order pi that the fp8 kernel's 64-deep PV product
+// needs.
 //
 // The cached state is the clean K/V of each generated chunk, kept for the
 // chunks that follow (discuss.pytorch.kr "JoyAI-Video-Edit 소개", real-time
@@ -27,6 +29,12 @@ constexpr int kThreads = 256;
 // key stored in V column p of a tile: swap bits 2 and 3 (an involution)
 __device__ __forceinline__ int kappa(int p) {
   return (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+// fp8 rings: key stored in V column p (0..63) of a 64-key tile, the order in
+// which the fp8 attention kernel's accumulators hand keys to its 64-deep PV
+// product (bit permutation: key bits 5,4,3,2 = p bits 4,3,2,5)
+__device__ __forceinline__ int pi64(int p) {
+  return ((p & 0x1C) << 1) | ((p & 0x20) >> 3) | (p & 3);
 }
 
 // ---------------------------------------------------------------- bf16 ----
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
       uint32_t x = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        x |= static_cast<uint32_t>(vtile[kappa(ch * 16 + 4 * j + b) * kLdsPitch + dd]) << (8 * b);
+        x |= static_cast<uint32_t>(vtile[pi64(ch * 16 + 4 * j + b) * kLdsPitch + dd]) << (8 * b);
       w[j] = x;
     }
     st16(vtd + (static_cast<size_t>(h) * D + dd) * pitch + r0 + ch * 16,

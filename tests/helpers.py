@@ -55,6 +55,7 @@ class StreamRun:
         self.ring = ring
         self.fp8 = fp8
         self.heads = heads
+        self.last_vmax = 0.0     # largest |v| of the current chunk's staged values
         ck, cv = stream.kv_cond() if self.w.cond_tokens else (None, None)
         self.oracle = O1.StreamOracle(self.w.window, self.w.scale,
                                       self._ref(ck), self._ref(cv))
@@ -79,6 +80,7 @@ class StreamRun:
         for step in range(self.w.steps):
             k, v = self.s.kv_noisy(t, step)
             q = self.s.q(t, step)
+            self.last_vmax = float(np.abs(self._ref(v)).max())
             self.ring.stage(k.cuda(), v.cuda())
             lse_t = torch.empty(self.w.heads, self.w.chunk_tokens, dtype=torch.float32,
                                 device="cuda") if lse else None

@@ -1,0 +1,222 @@
+"""GPU parity of the fp8 (E4M3) KV path.
+
+- K1 on an fp8 ring: codes and per-(head, segment) scales bit for bit equal
+  to the oracle's encoder (O3), V columns in the documented tile order.
+- Attention over an fp8 ring against the fp64 oracle run on the dequantised
+  K/V (the values the ring holds, computed by O3 from the same bf16 inputs):
+  max-abs <= 6e-2 over the whole output of a call.  Q stays bf16 at the
+  boundary; the kernel's own fp8 rounding of Q and P is part of the error.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_attention_amd as kv
+import synth
+from helpers import StreamRun, compare, fp8_roundtrip_tokens
+from oracle import attention as O1
+from oracle import fp8 as O3
+
+pytestmark = pytest.mark.gpu
+
+FP8_MAX_ABS = 6e-2
+
+
+def pi64(p):
+    return ((p & 0x1C) << 1) | ((p & 0x20) >> 3) | (p & 3)
+
+
+def fp8_ring(w):
+    return kv.Ring(w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window,
+                   kv_dtype="fp8_e4m3")
+
+
+def fp8_workload(w, **kw):
+    return dataclasses.replace(w, kv_dtype="fp8_e4m3", **kw)
+
+
+@pytest.mark.parametrize("H,d,n,m", [(3, 128, 100, 40), (2, 64, 64, 16), (40, 128, 1620, 256),
+                                     (1, 128, 1, 1)])
+def test_cache_write_fp8_is_bit_exact(H, d, n, m):
+    w = synth.Workload("k1f8", H, d, n, m, 1, 3, kv_dtype="fp8_e4m3", seed=7)
+    s = synth.Stream(w, "sharp")
+    r = fp8_ring(w)
+    ck, cv = s.kv_cond()
+    r.cond(ck.cuda(), cv.cuda())
+    k, v = s.kv_noisy(0)
+    r.stage(k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    for which, (kk, vv) in ((-1, (ck, cv)), (-2, (k, v))):
+        K, Vt, ks, vs, rows = r.slot_tensors(which)
+        K, Vt = K.cpu().numpy(), Vt.cpu().numpy()
+        ks, vs = ks.cpu().numpy(), vs.cpu().numpy()
+        kc, ksc = O3.quantize_segment(kk.float().numpy())
+        vc, vsc = O3.quantize_segment(vv.float().numpy())
+        assert rows == kk.shape[0]
+        assert np.array_equal(ks.view(np.uint32), ksc.view(np.uint32))
+        assert np.array_equal(vs.view(np.uint32), vsc.view(np.uint32))
+        P = K.shape[1]
+        assert np.array_equal(K[:, :rows], kc.transpose(1, 0, 2))
+        assert (K[:, rows:] == 0).all()
+        p = np.arange(P)
+        key = (p // 64) * 64 + pi64(p % 64)
+        vpad = np.zeros((P, H, d), np.uint8)
+        vpad[:rows] = vc
+        assert np.array_equal(Vt, vpad[key].transpose(1, 2, 0))
+
+
+# Peaky inputs (logit std ~4: a few keys carry almost all the weight) are not
+# one of the measured configurations.  For them the bound comes from the
+# arithmetic: the kernel rounds each p to E4M3, p~ = p (1 + d) with |d| <= u =
+# 2^-4, and normalises by the sum of the same rounded values, so
+# |O~ - O| <= ((1 + u) / (1 - u) - 1) max|v| = 0.1333 max|v| (Q's own rounding
+# adds well under 1% at these logits).
+P8_U = 2.0 ** -4
+P8_BOUND = (1 + P8_U) / (1 - P8_U) - 1
+
+
+def check_fp8(st, what, dist="sharp", vmax=None):
+    assert st["finite"], what
+    if dist == "peaky":
+        assert st["max_abs"] <= P8_BOUND * vmax, f"{what}: {st} (bound {P8_BOUND * vmax:.3f})"
+        assert st["rel_l2"] <= 2.5e-2, f"{what}: {st}"
+    else:
+        assert st["max_abs"] <= FP8_MAX_ABS, f"{what}: {st}"
+
+
+def visible_vmax(run):
+    """largest |v| the oracle's current stream state holds (dequantised)"""
+    o = run.oracle
+    vals = [np.abs(o.cond_v).max()] if o.cond_v is not None else []
+    vals += [np.abs(v).max() for _, v in o.clean.values()]
+    return float(max(vals)) if vals else 0.0
+
+
+@pytest.mark.parametrize("dist", ["baseline", "sharp", "peaky"])
+def test_tiny_stream_fp8(dist):
+    w = fp8_workload(synth.WORKLOADS["tiny"])
+    run = StreamRun(synth.Stream(w, dist), fp8_ring(w), fp8=True)
+    worst = 0.0
+    for t in range(w.chunks):
+        (o, ref, st), = run.chunk(t, lse=True)
+        vmax = max(visible_vmax(run), run.last_vmax)
+        check_fp8(st, f"tiny fp8 {dist} t={t}", dist, vmax)
+        worst = max(worst, st["rel_l2"])
+        assert st["lse_max_abs"] < 5e-2, st
+    print(f"tiny fp8 {dist}: worst rel-L2 {worst:.3e}")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(heads=2, head_dim=128, chunk_tokens=1, cond_tokens=0, window=0),
+    dict(heads=3, head_dim=128, chunk_tokens=63, cond_tokens=5, window=1),
+    dict(heads=1, head_dim=128, chunk_tokens=129, cond_tokens=64, window=2),
+    dict(heads=4, head_dim=64, chunk_tokens=200, cond_tokens=1, window=3),
+    dict(heads=5, head_dim=128, chunk_tokens=64, cond_tokens=128, window=0),
+])
+@pytest.mark.parametrize("dist", ["sharp", "peaky"])
+def test_edge_shapes_fp8(shape, dist):
+    w = synth.Workload("edge8", chunks=shape["window"] + 4, seed=13, kv_dtype="fp8_e4m3",
+                       **shape)
+    run = StreamRun(synth.Stream(w, dist), fp8_ring(w), fp8=True)
+    for t in range(w.chunks):
+        (o, ref, st), = run.chunk(t)
+        vmax = max(visible_vmax(run), run.last_vmax)
+        check_fp8(st, f"{shape} {dist} t={t}", dist, vmax)
+
+
+@pytest.mark.parametrize("dist", ["baseline", "sharp"])
+def test_fp8_config_stream_sampled(dist):
+    # the fp8 configuration (720p shape, W = 3, E4M3 K/V with per-head,
+    # per-segment scales, Q bf16): chunks 0..5 on 3 heads, GPU on all 40
+    w = synth.WORKLOADS["fp8"]
+    heads = [0, 17, 39]
+    run = StreamRun(synth.Stream(w, dist), fp8_ring(w), fp8=True, heads=heads)
+    for t in range(6):
+        (o, ref, st), = run.chunk(t, lse=True)
+        check_fp8(st, f"fp8 cfg {dist} t={t}")
+        print(f"fp8 cfg {dist} t={t}: max-abs {st['max_abs']:.2e} rel-L2 {st['rel_l2']:.2e}")
+
+
+@pytest.mark.parametrize("where", ["cond", "current"])
+@pytest.mark.parametrize("shift", [30.0, -30.0, 80.0])
+def test_fp8_segment_offset_stress(where, shift):
+    # logits against one segment shifted by `shift`: large logits after the
+    # first keys make the kernel recompute with the true max (fp8 P would
+    # saturate otherwise)
+    w = synth.Workload("stress8", 4, 128, 200, 70, 2, 4, seed=29, kv_dtype="fp8_e4m3")
+    s = synth.Stream(w, "sharp")
+    r = fp8_ring(w)
+    ck, cv = s.kv_cond()
+    ckr = synth.zero_feature0(ck)
+    if where == "cond":
+        _, ckr = synth.offset_segment(s.q(0), ck, shift, w.scale)
+    r.cond(ckr.cuda(), cv.cuda())
+    so = O1.StreamOracle(w.window, w.scale, fp8_roundtrip_tokens(ckr), fp8_roundtrip_tokens(cv))
+    for t in range(w.chunks):
+        k, v = s.kv_noisy(t)
+        q = s.q(t).clone()
+        q[..., 0] = 1.0
+        if where == "current":
+            _, k = synth.offset_segment(q, k, shift, w.scale)
+        else:
+            k = synth.zero_feature0(k)
+        r.stage(k.cuda(), v.cuda())
+        o = r.attention(q.cuda())
+        ref, _ = so.attend(t, O1.as_f64(q), fp8_roundtrip_tokens(k), fp8_roundtrip_tokens(v))
+        check_fp8(compare(o, ref), f"fp8 stress {where} {shift} t={t}")
+        kc, vc = s.kv_clean(t)
+        kc = synth.zero_feature0(kc)
+        r.commit(kc.cuda(), vc.cuda())
+        so.commit(t, fp8_roundtrip_tokens(kc), fp8_roundtrip_tokens(vc))
+        r.evict()
+
+
+def test_fp8_segments_with_different_value_scales():
+    # condition values 20x larger and current values 20x smaller than the
+    # rest: the kernel carries O across segments with different V scales.
+    # Tolerance relative to the output's magnitude (values up to ~20 here).
+    w = synth.Workload("vscale8", 3, 128, 150, 90, 2, 4, seed=31, kv_dtype="fp8_e4m3")
+    s = synth.Stream(w, "sharp")
+    r = fp8_ring(w)
+    ck, cv = s.kv_cond()
+    cv = (cv.float() * 20).to(torch.bfloat16)
+    r.cond(ck.cuda(), cv.cuda())
+    so = O1.StreamOracle(w.window, w.scale, fp8_roundtrip_tokens(ck), fp8_roundtrip_tokens(cv))
+    for t in range(w.chunks):
+        k, v = s.kv_noisy(t)
+        v = (v.float() / 20).to(torch.bfloat16)
+        q = s.q(t)
+        r.stage(k.cuda(), v.cuda())
+        o = r.attention(q.cuda())
+        ref, _ = so.attend(t, O1.as_f64(q), fp8_roundtrip_tokens(k), fp8_roundtrip_tokens(v))
+        st = compare(o, ref)
+        scale = max(1.0, float(np.abs(ref).max()))
+        assert st["finite"] and st["max_abs"] <= FP8_MAX_ABS * scale, (t, st, scale)
+        kc, vc = s.kv_clean(t)
+        r.commit(kc.cuda(), vc.cuda())
+        so.commit(t, fp8_roundtrip_tokens(kc), fp8_roundtrip_tokens(vc))
+        r.evict()
+
+
+def test_fp8_repeat_runs_are_bitwise_deterministic():
+    w = synth.WORKLOADS["fp8"]
+    s = synth.Stream(w, "baseline")
+    r = fp8_ring(w)
+    ck, cv = s.kv_cond()
+    r.cond(ck.cuda(), cv.cuda())
+    for t in range(5):
+        k, v = s.kv_noisy(t)
+        r.stage(k.cuda(), v.cuda())
+        if t == 4:
+            q = s.q(t).cuda()
+            lse1 = torch.empty(w.heads, w.chunk_tokens, dtype=torch.float32, device="cuda")
+            lse2 = torch.empty_like(lse1)
+            o1 = r.attention(q, lse=lse1).clone()
+            o2 = r.attention(q, lse=lse2)
+            assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+            assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+        kc, vc = s.kv_clean(t)
+        r.commit(kc.cuda(), vc.cuda())
+        r.evict()
