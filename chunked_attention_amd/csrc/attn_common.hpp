@@ -109,6 +109,40 @@ __device__ __forceinline__ void wait_vm_keep_lds_done() {
 }
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
+// LDS tiles are stored as rows of RB bytes in 16-byte chunks; logical chunk c
+// of row r sits at physical chunk swz_chunk<RB>(r, c) (an XOR, so the same
+// function maps back).  gfx950's LDS serves a 128-bit read for 16 lanes (256
+// bytes over 64 banks of 4 bytes) per clock; when 16 lanes read the same
+// logical chunk of 16 consecutive rows, these swizzles put the 16 physical
+// chunks in 16 distinct 16-byte bank groups of a 256-byte period.  All three
+// repeat every 16 rows.
+template <int RB>
+__device__ __forceinline__ int swz_chunk(int r, int c) {
+  static_assert(RB == 256 || RB == 128 || RB == 64, "row size");
+  if constexpr (RB == 256) return c ^ (r & 15);
+  else if constexpr (RB == 128) return c ^ ((r >> 1) & 7);
+  else return c ^ ((r >> 2) & 3);
+}
+template <int RB>
+__device__ __forceinline__ uint32_t swz_off(int r, int c) {
+  return static_cast<uint32_t>(r * RB + swz_chunk<RB>(r, c) * 16);
+}
+constexpr int kSwizzleRows = 16;
+
+// a ^ imm, computed where it is used: the asm keeps the compiler from
+// hoisting one register per immediate out of the loop (the reads of one
+// operand differ only by such an XOR, see swz_chunk)
+template <uint32_t kImm>
+__device__ __forceinline__ uint32_t xor_here(uint32_t a) {
+  if constexpr (kImm == 0) {
+    return a;
+  } else {
+    uint32_t r;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "i"(kImm), "v"(a));
+    return r;
+  }
+}
+
 // Workgroup barrier without a memory fence (a fence would make the compiler
 // wait for every copy in flight).  Written as an asm statement with a memory
 // clobber so that no memory access is moved across it at any compiler level;

@@ -26,10 +26,10 @@
 // in register i; the ring stores V's key columns in exactly that order within
 // each group of 16 (kappa, a swap of index bits 2 and 3), so the 8 keys a
 // lane feeds to one PV step are consecutive and each Vt operand is one
-// 16-byte LDS read.  Tiles are XOR-swizzled per row (16-byte chunk c of row r
-// lives at c ^ (r & 7)) so 8 consecutive lanes' 16-byte reads hit distinct
-// bank groups; the swizzle depends only on the lane, so the unrolled reads of
-// one lane differ by immediate offsets.  K and Vt tiles are copied from
+// 16-byte LDS read.  Tiles are XOR-swizzled per row (swz_chunk in
+// attn_common.hpp) so the 16 lanes an LDS clock serves hit distinct bank
+// groups; the swizzle depends only on the lane, so the unrolled reads of one
+// lane differ by immediate offsets.  K and Vt tiles are copied from
 // global memory straight into LDS (buffer_load ... lds, scalar base and
 // offset, per-lane 32-bit offset), two buffers each.
 //
@@ -96,24 +96,25 @@ void attn_fwd_bf16(const AttnArgs a) {
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // Per-lane byte offsets of the copies.  K: a 1 KB block holds 1024 / (2D)
-  // consecutive key rows; lane l fills 16-byte chunk l % (D/8) of row
-  // l / (D/8), which takes logical chunk pc ^ (row & 7).  The row's low 3
-  // bits depend on the block only through its parity (D = 128) or not at all
-  // (D = 64).  Vt: a 1 KB block holds 8 rows d of 128 bytes; lane l fills
-  // chunk l % 8 of row l / 8 with logical chunk (l % 8) ^ (l / 8).
+  // Per-lane byte offsets of the copies (16 bytes per lane, 1 KB per wave
+  // instruction).  K: a block holds 1024 / (2D) rows of 2D bytes; lane l
+  // fills physical chunk l % (D/8) of row l / (D/8) and fetches the logical
+  // chunk the swizzle puts there.  Vt: a block holds 8 rows of 128 bytes.
+  // Each wave's blocks start on a multiple of 16 rows, so copy u of a wave
+  // sees the same swizzle phase in every wave.
   constexpr int kKLanesPerRow = D / 8;
   constexpr int kKRowsPerBlk = 1024 / G::kKRow;
-  static_assert(kKRowsPerBlk == 8 || (G::kKInstr % 2) == 0, "row parity per block");
-  uint32_t koff[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int row = par * kKRowsPerBlk + lane / kKLanesPerRow;
-    const int pc = lane % kKLanesPerRow;
-    koff[par] = (lane / kKLanesPerRow) * G::kKRow + ((pc ^ (row & 7)) * 16);
-  }
+  static_assert(G::kKInstr * kKRowsPerBlk % kSwizzleRows == 0, "K swizzle phase per copy");
+  static_assert(G::kVInstr * 8 % kSwizzleRows == 0, "Vt swizzle phase per copy");
+  // Copy u (in 0..3) of a wave covers rows whose swizzle phase differs from
+  // copy 0's by u << 2 in the chunk index for both K row sizes (rows 4u.. of
+  // 256 bytes: r & 15 gains 4u; rows 8u.. of 128 bytes: (r >> 1) & 7 gains
+  // 4u), i.e. by u << 6 in the byte offset; likewise the Vt copies by
+  // (u & 1) << 6.
+  const uint32_t koff0 = (lane / kKLanesPerRow) * G::kKRow +
+                         swz_chunk<G::kKRow>(lane / kKLanesPerRow, lane % kKLanesPerRow) * 16;
   const uint32_t vrow = lane >> 3;
-  const uint32_t vchunk16 = (((lane & 7) ^ vrow) & 7) * 16;
+  const uint32_t vchunk0 = swz_chunk<128>(lane >> 3, lane & 7) * 16;
 
   // copies of one tile into LDS buffer DST; this wave's share of the 1 KB
   // blocks
@@ -123,30 +124,32 @@ void attn_fwd_bf16(const AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < G::kKInstr; ++u) {
       const int blk = wave * G::kKInstr + u;
-      // the block's row parity: kKInstr is even for D = 128, and D = 64 has
-      // 8 rows per block
-      const int par = kKRowsPerBlk == 4 ? (u & 1) : 0;
-      dma16(c.rk, buf(DST) + blk * 1024, koff[par], sbase + blk * 1024);
+      dma16(c.rk, buf(DST) + blk * 1024, koff0 ^ (u << 6), sbase + blk * 1024);
     }
   };
   auto dma_v = [&](auto dst_tag, const TileCursor& c) {
     constexpr int DST = decltype(dst_tag)::value;
     const uint32_t pitch2 = static_cast<uint32_t>(c.pitch) * 2;
-    const uint32_t voff = vrow * pitch2 + vchunk16;
+    const uint32_t voff = vrow * pitch2 + vchunk0;
 #pragma unroll
     for (int u = 0; u < G::kVInstr; ++u) {
       const int blk = wave * G::kVInstr + u;
-      dma16(c.rv, buf(DST) + blk * 1024, voff,
+      dma16(c.rv, buf(DST) + blk * 1024, voff ^ ((u & 1) << 6),
             static_cast<uint32_t>(blk) * 8 * pitch2 + static_cast<uint32_t>(c.k0) * 2);
     }
   };
 
+  // LDS reads.  Logical chunk ks*2 + half of row r sits at chunk
+  // (half ^ s(r)) ^ (ks*2), so each read is one per-lane offset XORed with
+  // ks << 5 (bits 5..7; row offsets and buffer bases leave them clear).
+  const uint32_t krd = col * G::kKRow + swz_chunk<G::kKRow>(col, half) * 16;
+  const uint32_t vrd = col * 128 + swz_chunk<128>(col, half) * 16;
   // K operands of one 32-key half tile: rows col of the half at kl
   auto read_kops = [&](const unsigned char* kl, bf16x8_t (&kops)[kDS]) {
-    const unsigned char* rowp = kl + col * G::kKRow;
-#pragma unroll
-    for (int ks = 0; ks < kDS; ++ks)
-      kops[ks] = *reinterpret_cast<const bf16x8_t*>(rowp + (((ks * 2 + half) ^ (col & 7)) * 16));
+    kvc::static_for<kDS>([&](auto ks_tag) {
+      constexpr int ks = decltype(ks_tag)::value;
+      kops[ks] = *reinterpret_cast<const bf16x8_t*>(kl + xor_here<ks * 32>(krd));
+    });
   };
   auto qk = [&](const bf16x8_t (&kops)[kDS], const bf16x8_t (&qreg)[kDS], f32x16_t& s) {
 #pragma unroll
@@ -273,14 +276,14 @@ void attn_fwd_bf16(const AttnArgs a) {
           read_kops(buf(KN), kops);
         }
         bf16x8_t vops[2][kDB];
+        kvc::static_for<2>([&](auto pp_tag) {
+          constexpr int pp = decltype(pp_tag)::value;
+          // key chunk (HH*2 + pp)*2 + half of rows db*32 + col
+          const uint32_t vo = xor_here<(HH * 2 + pp) * 32>(vrd);
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-          for (int db = 0; db < kDB; ++db) {
-            const int ps = HH * 2 + pp;
-            vops[pp][db] = *reinterpret_cast<const bf16x8_t*>(
-                buf(VJ) + (db * 32 + col) * 128 + (((ps * 2 + half) ^ (col & 7)) * 16));
-          }
+          for (int db = 0; db < kDB; ++db)
+            vops[pp][db] = *reinterpret_cast<const bf16x8_t*>(buf(VJ) + db * 4096 + vo);
+        });
 
         f32x16_t& sc = sacc[CUR];
         mask(sc, cj.rows - cj.k0 - HH * 32);

@@ -33,9 +33,8 @@
 //   (at most once per segment, W+3 times per row), and by the last scale at
 //   the end.
 // Layout of the fp8 tiles in LDS: K rows of D bytes and Vt rows of 64 bytes,
-// 16-byte chunks XOR-swizzled so that 8 consecutive lanes' 16-byte reads hit
-// distinct bank groups: for 128-byte rows chunk c of row r lives at
-// c ^ (r & 7), for 64-byte rows at c ^ ((r >> 1) & 3).  The ring stores the
+// 16-byte chunks XOR-swizzled (swz_chunk in attn_common.hpp) so that the 16
+// lanes an LDS clock serves hit distinct bank groups.  The ring stores the
 // Vt columns of every 64-key tile in the order pi: column p holds key
 // ((p & 0x1C) << 1) | ((p & 0x20) >> 3) | (p & 3), which is the key a
 // lane's accumulator register delivers to B-operand byte p % 32 of lane half
@@ -63,14 +62,6 @@ struct Geo8 {
   static_assert(kKInstr >= 1 && kVInstr >= 1, "whole 1 KB copies per wave");
 };
 
-// byte offset of logical 16-byte chunk c of row r in a swizzled LDS tile
-// with rows of RB bytes
-template <int RB>
-__device__ __forceinline__ uint32_t swz(int r, int c) {
-  static_assert(RB == 128 || RB == 64, "row size");
-  if constexpr (RB == 128) return static_cast<uint32_t>(r * 128 + ((c ^ (r & 7)) * 16));
-  else return static_cast<uint32_t>(r * 64 + ((c ^ ((r >> 1) & 3)) * 16));
-}
 
 __device__ __forceinline__ i32x8_t ld32(const unsigned char* p0, const unsigned char* p1) {
   const uint4 a = *reinterpret_cast<const uint4*>(p0);
@@ -126,12 +117,18 @@ void attn_fwd_fp8(const AttnArgs a) {
   // swizzle puts there; the swizzle of a row depends on the lane only.  Vt:
   // a 1 KB block holds 16 rows of 64 bytes.
   constexpr int kKLanesPerRow = D / 16;
-  const int krow = lane / kKLanesPerRow;
-  const int kpc = lane % kKLanesPerRow;
-  const int klog = D == 128 ? (kpc ^ (krow & 7)) : (kpc ^ ((krow >> 1) & 3));
-  const uint32_t koff = static_cast<uint32_t>(krow * D + klog * 16);
+  constexpr int kKRowsPerBlk = 1024 / D;
+  static_assert(G::kKInstr * kKRowsPerBlk % kSwizzleRows == 0, "K swizzle phase per copy");
+  static_assert(G::kVInstr * 16 % kSwizzleRows == 0, "Vt swizzle phase per copy");
+  uint32_t koff[G::kKInstr];
+#pragma unroll
+  for (int u = 0; u < G::kKInstr; ++u) {
+    const int row = u * kKRowsPerBlk + lane / kKLanesPerRow;
+    koff[u] = static_cast<uint32_t>((lane / kKLanesPerRow) * D +
+                                    swz_chunk<D>(row, lane % kKLanesPerRow) * 16);
+  }
   const int vrow = lane >> 2;
-  const int vlog = (lane & 3) ^ ((vrow >> 1) & 3);
+  const int vlog = swz_chunk<64>(vrow, lane & 3);
 
   auto dma_k = [&](auto dst_tag, const TileCursor& c) {
     constexpr int DST = decltype(dst_tag)::value;
@@ -139,7 +136,7 @@ void attn_fwd_fp8(const AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < G::kKInstr; ++u) {
       const int blk = wave * G::kKInstr + u;
-      dma16(c.rk, buf(DST) + blk * 1024, koff, sbase + blk * 1024);
+      dma16(c.rk, buf(DST) + blk * 1024, koff[u], sbase + blk * 1024);
     }
   };
   auto dma_v = [&](auto dst_tag, const TileCursor& c) {
@@ -160,7 +157,7 @@ void attn_fwd_fp8(const AttnArgs a) {
     const int r = hh * 32 + col;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks)
-      kops[ks] = ld32(kt + swz<D>(r, ks * 4 + half * 2), kt + swz<D>(r, ks * 4 + half * 2 + 1));
+      kops[ks] = ld32(kt + swz_off<D>(r, ks * 4 + half * 2), kt + swz_off<D>(r, ks * 4 + half * 2 + 1));
   };
   // scores: K . (Q8hi + Q8lo / 16)^T
   auto qk = [&](const i32x8_t (&kops)[kKS], const i32x8_t (&qhi)[kKS], const i32x8_t (&qlo)[kKS],
@@ -358,7 +355,7 @@ void attn_fwd_fp8(const AttnArgs a) {
 #pragma unroll
           for (int db = 0; db < kDB; ++db) {
             const int rr = db * 32 + col;
-            const i32x8_t vops = ld32(vt + swz<64>(rr, half * 2), vt + swz<64>(rr, half * 2 + 1));
+            const i32x8_t vops = ld32(vt + swz_off<64>(rr, half * 2), vt + swz_off<64>(rr, half * 2 + 1));
             oacc[db] = mfma8(vops, pb, oacc[db]);
           }
           lacc = mfma8(ones, pb, lacc);

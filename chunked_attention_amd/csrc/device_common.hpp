@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
+#include <utility>
 
 namespace kvc {
 
@@ -34,6 +36,16 @@ __device__ __forceinline__ void st16(void* p, uint4 v) {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
   return __uint_as_float(b << 16);
+}
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace kvc
