@@ -22,12 +22,12 @@ namespace kvc {
 namespace attn {
 
 constexpr int kBq = kAttnRowQueries;    // queries per row (128)
-constexpr int kBk = kTileKeys;          // keys per tile (64)
+constexpr int kBk = kTileKeys;          // keys per stored tile (64): segment padding
 constexpr int kWaves = 4;               // waves per workgroup, 32 queries each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 32;                 // queries per wave
 constexpr int kMaxWg = kAttnMaxWg;      // persistent workgroups at most (2 per CU)
-constexpr int kMinPieceTiles = 16;      // smallest share of a row worth splitting off
+constexpr int kMinPieceKeys = 1024;    // smallest share of a row worth splitting off
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMl = 3 * 32;             // per wave: (reference, sum, exact sum) per query
@@ -40,7 +40,7 @@ struct SegArg {
   const float* vs;          // [H] V scales (fp8 rings)
   int rows;
   int pitch;
-  int tile0;                // first tile of this segment in the row's tile list
+  int tile0;                // first step of this segment in the row's step list
   int pad_;
 };
 
@@ -55,7 +55,7 @@ struct AttnArgs {
   int heads;
   float c;                  // softmax scale * log2(e)
   int nseg;
-  int ntiles;               // tiles per row (T)
+  int ntiles;               // steps per row (T; a step is a kernel-defined key count)
   int nqt;                  // rows per head
   int nrows;                // heads * nqt
   int nwg;                  // persistent workgroups
@@ -152,14 +152,14 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// Cursor over one row's key tiles: segment, first key of the tile, and that
-// segment's fields, all wave-uniform (scalar registers).  Moving to the next
-// tile touches no memory except when a segment ends.  E = bytes per stored
-// element.
+// Cursor over one row's key steps (SK keys each): segment, first key of the
+// step, and that segment's fields, all wave-uniform (scalar registers).
+// Moving to the next step touches no memory except when a segment ends.
+// E = bytes per stored element.
 struct TileCursor {
-  int t;                    // tile index within the row
+  int t;                    // step index within the row
   int s;                    // segment
-  int k0;                   // first key of the tile within the segment
+  int k0;                   // first key of the step within the segment
   int rows;
   int pitch;
   __amdgpu_buffer_rsrc_t rk;   // this head's K plane of the segment
@@ -175,21 +175,21 @@ __device__ __forceinline__ void cursor_fields(const AttnArgs& a, TileCursor& c, 
   c.rk = make_rsrc(s.k + static_cast<size_t>(h) * plane, plane);
   c.rv = make_rsrc(s.vt + static_cast<size_t>(h) * plane, plane);
 }
-template <int D, int E>
+template <int D, int E, int SK>
 __device__ __forceinline__ void cursor_seek(const AttnArgs& a, TileCursor& c, int t, int h) {
   int s = 0;
   while (s + 1 < a.nseg && a.seg[s + 1].tile0 <= t) ++s;
   c.t = t;
   c.s = s;
-  c.k0 = (t - a.seg[s].tile0) * kBk;
+  c.k0 = (t - a.seg[s].tile0) * SK;
   cursor_fields<D, E>(a, c, h);
 }
-// one tile on, but never past tile `last`
-template <int D, int E>
+// one step on, but never past step `last`
+template <int D, int E, int SK>
 __device__ __forceinline__ void cursor_next(const AttnArgs& a, TileCursor& c, int last, int h) {
   if (c.t >= last) return;
   ++c.t;
-  c.k0 += kBk;
+  c.k0 += SK;
   if (c.k0 >= c.rows) {
     ++c.s;
     c.k0 = 0;
@@ -356,9 +356,10 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
     a.lse[static_cast<size_t>(h) * a.n + qi] = (m_run + __log2f(le_tot)) * kLn2;
 }
 
-// Host side: kernel arguments from a launch description (segment table,
-// tiles, rows, grid, workspace).  Returns KVC_OK or KVC_E_INVAL.
-kvc_status fill_args(const AttnDesc& d, AttnArgs& a);
+// Host side: kernel arguments from a launch description (segment table in
+// steps of step_keys keys, rows, grid, workspace).  Returns KVC_OK or
+// KVC_E_INVAL.
+kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a);
 // zero `n` words on the stream (a kernel, not a memset: capturable)
 void launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t stream);
 

@@ -8,19 +8,19 @@
 // sink).  The visible set is never concatenated: the kernel walks the ring's
 // segment table (cache slots in logical order) tile by tile.
 //
-// Work: a "row" is 128 queries of one head; its keys are T tiles of 64 keys
-// over all segments (a segment's last tile is masked).  A workgroup runs one
+// Work: a "row" is 128 queries of one head; its keys are T steps of 32 keys
+// over all segments (a segment's last step is masked).  A workgroup runs one
 // row at a time with 4 waves of 32 queries; two workgroups share a CU, so
 // every SIMD holds two waves and interleaves one wave's softmax (VALU) with
 // the other's matrix products (MFMA).  The grid is persistent: nwg
-// workgroups (two per CU) split the R*T (row, tile) steps into equal
+// workgroups (two per CU) split the R*T (row, step) pairs into equal
 // contiguous ranges (stream-K), so the whole GPU stays busy whatever R is;
 // the split and the merge of split rows live in attn_common.hpp.
 //
-// Per tile and wave (32 queries), with 32x32x16 bf16 MFMAs (fp32
+// Per step and wave (32 keys x 32 queries), with 32x32x16 bf16 MFMAs (fp32
 // accumulate):
-//   S^T[64 keys x 32 q] = K_tile . Q^T      A = K from LDS, B = Q in VGPRs
-//   O^T[d x 32 q]      += Vt_tile . P^T     A = Vt from LDS, B = P in VGPRs
+//   S^T[32 keys x 32 q] = K_step . Q^T      A = K from LDS, B = Q in VGPRs
+//   O^T[d x 32 q]      += Vt_step . P^T     A = Vt from LDS, B = P in VGPRs
 // Computing transposed scores puts P^T straight into the B-operand layout of
 // the PV product.  The accumulator holds key rows (i/4)*8 + (lane/32)*4 + i%4
 // in register i; the ring stores V's key columns in exactly that order within
@@ -28,15 +28,15 @@
 // lane feeds to one PV step are consecutive and each Vt operand is one
 // 16-byte LDS read.  Tiles are XOR-swizzled per row (swz_chunk in
 // attn_common.hpp) so the 16 lanes an LDS clock serves hit distinct bank
-// groups; the swizzle depends only on the lane, so the unrolled reads of one
-// lane differ by immediate offsets.  K and Vt tiles are copied from
-// global memory straight into LDS (buffer_load ... lds, scalar base and
-// offset, per-lane 32-bit offset), two buffers each.
+// groups; the reads of one operand differ by an XOR of one per-lane offset.
+// K and Vt are copied from global memory straight into LDS (buffer_load ...
+// lds, scalar base and offset, per-lane 32-bit offset).
 //
-// Software pipeline: while the softmax of half tile u runs on the VALU, the
-// QK^T MFMAs of half tile u+1 are issued; then the PV MFMAs of half tile u.
-// So K runs one tile ahead of V: tile j reads K_{j+1} and V_j while K_{j+2}
-// and V_{j+1} stream in.
+// Software pipeline over steps of 32 keys, with K and Vt in rings of four
+// LDS slots each: while the softmax of step s runs on the VALU, the QK^T
+// MFMAs of step s+1 are issued, then the PV MFMAs of step s.  K copies run
+// four steps ahead and Vt copies three, so every copy has two steps to land;
+// one barrier per step.
 //
 // Softmax in base 2 with a fixed reference per row piece: t = s*scale*log2(e)
 // and p = 2^(t - m_ref), where m_ref is the max of the piece's first 32 keys,
@@ -55,17 +55,21 @@ namespace {
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 constexpr int kMaxPasses = 4;
 
-// Geometry of the bf16 tiles for head dim D.
+// Geometry of the bf16 pipeline for head dim D: steps of 32 keys; K and Vt
+// of a step each fill one LDS slot, four slots per ring.
 template <int D>
 struct Geo {
+  static constexpr int kStep = 32;                  // keys per step
   static constexpr int kKRow = 2 * D;               // bytes per K row
-  static constexpr int kKBytes = kBk * kKRow;       // K tile bytes
-  static constexpr int kVBytes = D * kBk * 2;       // Vt tile bytes (D rows of 128 B)
+  static constexpr int kKBytes = kStep * kKRow;     // K slot bytes
+  static constexpr int kVRow = 2 * kStep;           // bytes per Vt row (64)
+  static constexpr int kVBytes = D * kVRow;         // Vt slot bytes
   static constexpr int kKInstr = kKBytes / 1024 / kWaves;   // 1 KB copy per wave-instruction
   static constexpr int kVInstr = kVBytes / 1024 / kWaves;
   static constexpr int kDS = D / 16;                // k-steps over d for QK^T
   static constexpr int kDB = D / 32;                // 32-row blocks of O^T
-  static_assert(kKInstr >= 1 && kVInstr >= 1, "whole 1 KB copies per wave");
+  static constexpr int kSlots = 4;                  // ring slots for K and for Vt
+  static_assert(kKInstr >= 1 && kVInstr >= 1 && kKInstr == kVInstr, "copy counts");
 };
 
 template <int D, bool kLse>
@@ -74,17 +78,24 @@ void attn_fwd_bf16(const AttnArgs a) {
   using G = Geo<D>;
   constexpr int kDS = G::kDS;
   constexpr int kDB = G::kDB;
-  // LDS: two K tiles and two Vt tiles, as four separate arrays so that the
-  // compiler can tell reads of one buffer from copies landing in another
-  // (a single array would make it wait for every copy in flight before any
-  // LDS read).  kK0.. name the buffers.
-  constexpr int kK0 = 0, kK1 = 1, kV0 = 2, kV1 = 3;
+  constexpr int kStep = G::kStep;
+  // LDS: two rings of four slots (K, Vt), as eight separate arrays so that
+  // the compiler can tell reads of one slot from copies landing in another
+  // (one array would make it wait for every copy in flight before any LDS
+  // read).  Slot b of K is buffer b, slot b of Vt is buffer 4 + b.
   __shared__ __attribute__((aligned(1024))) unsigned char kb0[G::kKBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char kb1[G::kKBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb2[G::kKBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb3[G::kKBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vb0[G::kVBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vb1[G::kVBytes];
-  auto buf = [&](int b) -> unsigned char* {
-    return b == kK0 ? kb0 : b == kK1 ? kb1 : b == kV0 ? vb0 : vb1;
+  __shared__ __attribute__((aligned(1024))) unsigned char vb2[G::kVBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb3[G::kVBytes];
+  auto kslot = [&](int b) -> unsigned char* {
+    return b == 0 ? kb0 : b == 1 ? kb1 : b == 2 ? kb2 : kb3;
+  };
+  auto vslot = [&](int b) -> unsigned char* {
+    return b == 0 ? vb0 : b == 1 ? vb1 : b == 2 ? vb2 : vb3;
   };
   __shared__ unsigned s_ticket;
   __shared__ int s_vote[kWaves][2];
@@ -98,53 +109,47 @@ void attn_fwd_bf16(const AttnArgs a) {
 
   // Per-lane byte offsets of the copies (16 bytes per lane, 1 KB per wave
   // instruction).  K: a block holds 1024 / (2D) rows of 2D bytes; lane l
-  // fills physical chunk l % (D/8) of row l / (D/8) and fetches the logical
-  // chunk the swizzle puts there.  Vt: a block holds 8 rows of 128 bytes.
-  // Each wave's blocks start on a multiple of 16 rows, so copy u of a wave
-  // sees the same swizzle phase in every wave.
+  // fills physical chunk l % (D/8) of its row and fetches the logical chunk
+  // the swizzle puts there.  Copy u of wave w covers block w*kKInstr + u; its
+  // swizzle phase differs from copy 0's by u << 2 in the chunk index (4 rows
+  // of 256 bytes), i.e. by u << 6 in the byte offset.  Vt: a block holds 16
+  // rows of 64 bytes; the swizzle phase of a row is lane-only there.
   constexpr int kKLanesPerRow = D / 8;
   constexpr int kKRowsPerBlk = 1024 / G::kKRow;
-  static_assert(G::kKInstr * kKRowsPerBlk % kSwizzleRows == 0, "K swizzle phase per copy");
-  static_assert(G::kVInstr * 8 % kSwizzleRows == 0, "Vt swizzle phase per copy");
-  // Copy u (in 0..3) of a wave covers rows whose swizzle phase differs from
-  // copy 0's by u << 2 in the chunk index for both K row sizes (rows 4u.. of
-  // 256 bytes: r & 15 gains 4u; rows 8u.. of 128 bytes: (r >> 1) & 7 gains
-  // 4u), i.e. by u << 6 in the byte offset; likewise the Vt copies by
-  // (u & 1) << 6.
+  static_assert(G::kKInstr == 1 || kKRowsPerBlk == 4, "K copy phase by XOR");
+  const int krow0 = wave * G::kKInstr * kKRowsPerBlk + lane / kKLanesPerRow;
   const uint32_t koff0 = (lane / kKLanesPerRow) * G::kKRow +
-                         swz_chunk<G::kKRow>(lane / kKLanesPerRow, lane % kKLanesPerRow) * 16;
-  const uint32_t vrow = lane >> 3;
-  const uint32_t vchunk0 = swz_chunk<128>(lane >> 3, lane & 7) * 16;
+                         swz_chunk<G::kKRow>(krow0, lane % kKLanesPerRow) * 16;
+  const uint32_t vrow = lane >> 2;
+  const uint32_t vchunk = swz_chunk<G::kVRow>(vrow, lane & 3) * 16;
 
-  // copies of one tile into LDS buffer DST; this wave's share of the 1 KB
-  // blocks
   auto dma_k = [&](auto dst_tag, const TileCursor& c) {
     constexpr int DST = decltype(dst_tag)::value;
     const uint32_t sbase = static_cast<uint32_t>(c.k0) * G::kKRow;
 #pragma unroll
     for (int u = 0; u < G::kKInstr; ++u) {
       const int blk = wave * G::kKInstr + u;
-      dma16(c.rk, buf(DST) + blk * 1024, koff0 ^ (u << 6), sbase + blk * 1024);
+      dma16(c.rk, kslot(DST) + blk * 1024, koff0 ^ (u << 6), sbase + blk * 1024);
     }
   };
   auto dma_v = [&](auto dst_tag, const TileCursor& c) {
     constexpr int DST = decltype(dst_tag)::value;
     const uint32_t pitch2 = static_cast<uint32_t>(c.pitch) * 2;
-    const uint32_t voff = vrow * pitch2 + vchunk0;
+    const uint32_t voff = vrow * pitch2 + vchunk;
 #pragma unroll
     for (int u = 0; u < G::kVInstr; ++u) {
       const int blk = wave * G::kVInstr + u;
-      dma16(c.rv, buf(DST) + blk * 1024, voff ^ ((u & 1) << 6),
-            static_cast<uint32_t>(blk) * 8 * pitch2 + static_cast<uint32_t>(c.k0) * 2);
+      dma16(c.rv, vslot(DST) + blk * 1024, voff,
+            static_cast<uint32_t>(blk) * 16 * pitch2 + static_cast<uint32_t>(c.k0) * 2);
     }
   };
 
-  // LDS reads.  Logical chunk ks*2 + half of row r sits at chunk
-  // (half ^ s(r)) ^ (ks*2), so each read is one per-lane offset XORed with
-  // ks << 5 (bits 5..7; row offsets and buffer bases leave them clear).
+  // LDS reads.  Logical chunk 2j + half of row r sits at chunk
+  // (half ^ s(r)) ^ 2j, so each read is one per-lane offset XORed with j << 5
+  // (row offsets and slot bases leave those bits clear).
   const uint32_t krd = col * G::kKRow + swz_chunk<G::kKRow>(col, half) * 16;
-  const uint32_t vrd = col * 128 + swz_chunk<128>(col, half) * 16;
-  // K operands of one 32-key half tile: rows col of the half at kl
+  const uint32_t vrd = col * G::kVRow + swz_chunk<G::kVRow>(col, half) * 16;
+  // K operands of one step (rows col of the slot)
   auto read_kops = [&](const unsigned char* kl, bf16x8_t (&kops)[kDS]) {
     kvc::static_for<kDS>([&](auto ks_tag) {
       constexpr int ks = decltype(ks_tag)::value;
@@ -158,11 +163,11 @@ void attn_fwd_bf16(const AttnArgs a) {
     for (int ks = 0; ks < kDS; ++ks)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kops[ks], qreg[ks], s, 0, 0, 0);
   };
-  // the scores of one half tile with the padded keys of a segment's last
-  // tile set to -inf; `valid` = keys of this half that exist.  Register i
-  // holds key (i/4)*8 + half*4 + i%4.
+  // the scores of one step with the padded keys of a segment's last step
+  // set to -inf; `valid` = keys of this step that exist.  Register i holds
+  // key (i/4)*8 + half*4 + i%4.
   auto mask = [&](f32x16_t& sc, int valid) {
-    if (valid < 32) {
+    if (valid < kStep) {
       const int lim = valid - half * 4;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -171,8 +176,8 @@ void attn_fwd_bf16(const AttnArgs a) {
       }
     }
   };
-  // scaled max over the 32 keys of a half tile
-  auto half_max = [&](const f32x16_t& sc) -> float {
+  // scaled max over the 32 keys of a step
+  auto step_max = [&](const f32x16_t& sc) -> float {
     float mx = fmaxf(sc[0], sc[1]);
 #pragma unroll
     for (int i = 2; i < 16; ++i) mx = fmaxf(mx, sc[i]);
@@ -218,78 +223,73 @@ void attn_fwd_bf16(const AttnArgs a) {
       for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-      f32x16_t sacc[2];   // scores of a 32-key half tile, double-buffered
+      f32x16_t sacc[2];   // scores of a step, double-buffered
 
-      // cursors: tile j (scores, mask), tile j+1 (V copy), tile j+2 (K
-      // copy); the copy cursors stop at the piece's last tile, so every step
-      // issues the same number of copies (the extra ones land in a buffer
-      // that is not read again) and the vmcnt waits stay exact
+      // ---- prologue.  Ring slots are indexed by (step - t0) mod 4.  Copy
+      // K of steps t0..t0+3 and Vt of steps t0..t0+2 (in the order K0 V0 K1
+      // V1 K2 V2 K3; cursors stop at the piece's last step, so every slot
+      // copy happens and the vmcnt counts stay exact), wait for K0, V0, K1,
+      // and take the scores of step t0, whose max is the reference.
       TileCursor cj, cv, ck;
-      cursor_seek<D, 2>(a, cj, t0, h);
-      cv = cj;
-      cursor_next<D, 2>(a, cv, tlast, h);
-      ck = cv;
-      cursor_next<D, 2>(a, ck, tlast, h);
-
-      // ---- prologue: K_t0, V_t0, K_t0+1 in LDS; scores of the first half
-      // tile, whose max is the reference of the piece
+      cursor_seek<D, 2, kStep>(a, cj, t0, h);
       __syncthreads();
-      dma_k(std::integral_constant<int, kK0>{}, cj);
-      dma_v(std::integral_constant<int, kV0>{}, cj);
-      dma_k(std::integral_constant<int, kK1>{}, cv);
-      wait_dma();
+      ck = cj;
+      dma_k(std::integral_constant<int, 0>{}, ck);
+      dma_v(std::integral_constant<int, 0>{}, ck);
+      cursor_next<D, 2, kStep>(a, ck, tlast, h);
+      dma_k(std::integral_constant<int, 1>{}, ck);
+      dma_v(std::integral_constant<int, 1>{}, ck);
+      cursor_next<D, 2, kStep>(a, ck, tlast, h);
+      dma_k(std::integral_constant<int, 2>{}, ck);
+      dma_v(std::integral_constant<int, 2>{}, ck);
+      cv = ck;
+      cursor_next<D, 2, kStep>(a, cv, tlast, h);      // step t0+3: next V copy
+      cursor_next<D, 2, kStep>(a, ck, tlast, h);
+      dma_k(std::integral_constant<int, 3>{}, ck);
+      cursor_next<D, 2, kStep>(a, ck, tlast, h);      // step t0+4: next K copy
+      wait_vm_keep_lds_done<4 * G::kKInstr>();
       __syncthreads();
       {
         bf16x8_t kops[kDS];
-        read_kops(buf(kK0), kops);
+        read_kops(kslot(0), kops);
         qk(kops, qreg, sacc[0]);
       }
       if (pass == 0) {
         f32x16_t first = sacc[0];
         mask(first, cj.rows - cj.k0);
-        m_ref = half_max(first);
+        m_ref = step_max(first);
       }
+      // slot 0 of K is refilled by the first step: every wave's reads of it
+      // must be done
+      wait_vm_keep_lds_done<4 * G::kKInstr>();
+      barrier_no_fence();
 
-      // ---- one pipelined half step.  Half step u = 2i + hh covers keys
-      // [32 hh, 32 hh + 32) of tile j = t0 + i.  It issues the next copies,
-      // reads the operands it needs, computes the scores of half step u+1
-      // while running the softmax of half step u, then adds P V of half step u.
-      auto half_step = [&](auto u_tag) {
-        constexpr int U = decltype(u_tag)::value;     // u mod 4
-        constexpr int HH = U & 1;                      // which half of the tile
-        constexpr int TP = (U >> 1) & 1;               // parity of the tile
-        constexpr int CUR = U & 1;                     // score buffer of this half
-        constexpr int KJ = TP == 0 ? kK0 : kK1;        // K of tile j
-        constexpr int KN = TP == 0 ? kK1 : kK0;        // K of tile j+1
-        constexpr int VJ = TP == 0 ? kV0 : kV1;        // V of tile j
-        constexpr int VN = TP == 0 ? kV1 : kV0;        // V of tile j+1
-        if (HH == 0) {
-          dma_v(std::integral_constant<int, VN>{}, cv);   // V_{j+1}; V_{j-1} is done
-        } else {
-          dma_k(std::integral_constant<int, KJ>{}, ck);   // K_{j+2}; K_j is done
-        }
-        // operands: K rows of the next half step, Vt columns of this one
+      // ---- one pipelined step s (U = (s - t0) mod 4): copy K of step s+4
+      // (into the slot step s used) and Vt of step s+3 (into the slot step
+      // s-1 used); read K of step s+1 and Vt of step s; compute the scores
+      // of step s+1 while running the softmax of step s, then add P V.
+      auto step = [&](auto u_tag) {
+        constexpr int U = decltype(u_tag)::value;
+        constexpr int CUR = U & 1;
+        dma_k(std::integral_constant<int, U>{}, ck);
+        dma_v(std::integral_constant<int, (U + 3) & 3>{}, cv);
         bf16x8_t kops[kDS];
-        if (HH == 0) {
-          read_kops(buf(KJ) + 32 * G::kKRow, kops);
-        } else {
-          read_kops(buf(KN), kops);
-        }
+        read_kops(kslot((U + 1) & 3), kops);
         bf16x8_t vops[2][kDB];
         kvc::static_for<2>([&](auto pp_tag) {
           constexpr int pp = decltype(pp_tag)::value;
-          // key chunk (HH*2 + pp)*2 + half of rows db*32 + col
-          const uint32_t vo = xor_here<(HH * 2 + pp) * 32>(vrd);
+          // key chunk 2pp + half of Vt rows db*32 + col
+          const uint32_t vo = xor_here<pp * 32>(vrd);
 #pragma unroll
           for (int db = 0; db < kDB; ++db)
-            vops[pp][db] = *reinterpret_cast<const bf16x8_t*>(buf(VJ) + db * 4096 + vo);
+            vops[pp][db] = *reinterpret_cast<const bf16x8_t*>(vslot(U) + db * 32 * G::kVRow + vo);
         });
 
         f32x16_t& sc = sacc[CUR];
-        mask(sc, cj.rows - cj.k0 - HH * 32);
-        if (track_max) m_seen = fmaxf(m_seen, half_max(sc));
+        mask(sc, cj.rows - cj.k0);
+        if (track_max) m_seen = fmaxf(m_seen, step_max(sc));
 
-        // scores of the next half step (discarded after the last one)
+        // scores of the next step (discarded after the last one)
         qk(kops, qreg, sacc[1 - CUR]);
 
         // probabilities as bf16 P^T, and their row sums taken over the
@@ -330,34 +330,28 @@ void attn_fwd_bf16(const AttnArgs a) {
           for (int db = 0; db < kDB; ++db)
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vops[pp][db], pb[pp], oacc[db],
                                                               0, 0, 0);
-        // the copies issued one half step earlier must have landed (the ones
-        // just issued, of the other kind, may stay in flight) and this wave's
-        // LDS reads must be done before any wave starts overwriting buffers
-        if (HH == 0) {
-          wait_vm_keep_lds_done<G::kVInstr>();
-        } else {
-          wait_vm_keep_lds_done<G::kKInstr>();
-        }
+        // the next step reads K of step s+2 and Vt of step s+1 (copied two
+        // steps ago: only the last two steps' copies may stay in flight),
+        // and this wave's LDS reads must be done before any wave refills a
+        // slot
+        wait_vm_keep_lds_done<2 * (G::kKInstr + G::kVInstr)>();
         barrier_no_fence();
-        if (HH == 1) {
-          cursor_next<D, 2>(a, cj, tlast, h);
-          cursor_next<D, 2>(a, cv, tlast, h);
-          cursor_next<D, 2>(a, ck, tlast, h);
-        }
+        cursor_next<D, 2, kStep>(a, cj, tlast, h);
+        cursor_next<D, 2, kStep>(a, cv, tlast, h);
+        cursor_next<D, 2, kStep>(a, ck, tlast, h);
       };
 
       int j = t0;
-      for (; j + 1 < t1; j += 2) {
-        half_step(std::integral_constant<int, 0>{});
-        half_step(std::integral_constant<int, 1>{});
-        half_step(std::integral_constant<int, 2>{});
-        half_step(std::integral_constant<int, 3>{});
+      for (; j + 3 < t1; j += 4) {
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
       }
-      if (j < t1) {
-        half_step(std::integral_constant<int, 0>{});
-        half_step(std::integral_constant<int, 1>{});
-      }
-      // no copy may still land in a buffer the next pass or piece refills
+      if (j < t1) step(std::integral_constant<int, 0>{});
+      if (j + 1 < t1) step(std::integral_constant<int, 1>{});
+      if (j + 2 < t1) step(std::integral_constant<int, 2>{});
+      // no copy may still land in a slot the next pass or piece refills
       wait_dma();
 
       l_tot = xor32_sum(l_run);
@@ -389,7 +383,7 @@ void attn_fwd_bf16(const AttnArgs a) {
 template <int D>
 kvc_status launch_bf16(const AttnDesc& d, hipStream_t stream) {
   AttnArgs a;
-  const kvc_status st = fill_args(d, a);
+  const kvc_status st = fill_args(d, Geo<D>::kStep, a);
   if (st != KVC_OK) return st;
   if (!d.workspace_ready) launch_fill_u32(a.counters, 2 * a.nrows, 0u, stream);
   if (a.lse)
@@ -424,7 +418,7 @@ void launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t stream) {
   hipLaunchKernelGGL(fill_u32, dim3((n + 255) / 256), dim3(256), 0, stream, p, n, v);
 }
 
-kvc_status fill_args(const AttnDesc& d, AttnArgs& a) {
+kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a) {
   a.q = static_cast<const uint16_t*>(d.q);
   a.o = static_cast<uint16_t*>(d.o);
   a.lse = d.lse;
@@ -444,14 +438,14 @@ kvc_status fill_args(const AttnDesc& d, AttnArgs& a) {
     a.seg[s].pitch = d.seg[s].pitch;
     a.seg[s].tile0 = tiles;
     a.seg[s].pad_ = 0;
-    tiles += (d.seg[s].rows + kBk - 1) / kBk;
+    tiles += (d.seg[s].rows + step_keys - 1) / step_keys;
   }
   a.ntiles = tiles;
   a.nqt = (d.n + kBq - 1) / kBq;
   a.nrows = a.nqt * d.heads;
   a.total = static_cast<long long>(a.nrows) * a.ntiles;
   const long long slots = std::min(2 * device_cus(), kMaxWg);
-  const long long by_size = std::max<long long>(1, a.total / kMinPieceTiles);
+  const long long by_size = std::max<long long>(1, a.total * step_keys / kMinPieceKeys);
   a.nwg = static_cast<int>(std::min(slots, by_size));
   // workspace: counters, then partial reference/sums, then partial O
   unsigned char* ws = static_cast<unsigned char*>(d.workspace);

@@ -267,11 +267,11 @@ void attn_fwd_fp8(const AttnArgs a) {
       int pf[2][4];   // E4M3 P of the two half tiles: byte (i%4) of word i/4
 
       TileCursor cj, cv, ck;
-      cursor_seek<D, 1>(a, cj, t0, h);
+      cursor_seek<D, 1, kBk>(a, cj, t0, h);
       cv = cj;
-      cursor_next<D, 1>(a, cv, tlast, h);
+      cursor_next<D, 1, kBk>(a, cv, tlast, h);
       ck = cv;
-      cursor_next<D, 1>(a, ck, tlast, h);
+      cursor_next<D, 1, kBk>(a, ck, tlast, h);
       // softmax multiplier of the tile whose scores are being consumed
       auto ceff = [&](const TileCursor& c) { return cq * a.seg[c.s].ks[h]; };
 
@@ -367,9 +367,9 @@ void attn_fwd_fp8(const AttnArgs a) {
         }
         barrier_no_fence();
         if (HH == 1) {
-          cursor_next<D, 1>(a, cj, tlast, h);
-          cursor_next<D, 1>(a, cv, tlast, h);
-          cursor_next<D, 1>(a, ck, tlast, h);
+          cursor_next<D, 1, kBk>(a, cj, tlast, h);
+          cursor_next<D, 1, kBk>(a, cv, tlast, h);
+          cursor_next<D, 1, kBk>(a, ck, tlast, h);
         }
       };
 
@@ -408,7 +408,7 @@ void attn_fwd_fp8(const AttnArgs a) {
 template <int D>
 kvc_status launch_fp8_d(const AttnDesc& d, hipStream_t stream) {
   AttnArgs a;
-  const kvc_status st = fill_args(d, a);
+  const kvc_status st = fill_args(d, kBk, a);
   if (st != KVC_OK) return st;
   for (int s = 0; s < a.nseg; ++s)
     if (!a.seg[s].ks || !a.seg[s].vs) return KVC_E_INVAL;
