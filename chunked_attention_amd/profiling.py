@@ -25,6 +25,7 @@ import statistics
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCE = os.path.join(ROOT, "chunked_attention_amd", "csrc", "attn_fwd.hip")
 ATTN = "attn_fwd_bf16"
+ATTN8 = "attn_fwd_fp8"
 CALIB = "neg_kernel"
 
 
@@ -36,16 +37,28 @@ def _one(dirname: str, pattern: str) -> str:
 
 
 def short_name(name: str) -> str:
-    for key in (ATTN, "cache_write", "cache_amax", "cache_quant", "fill_u32", CALIB):
+    for key in (ATTN, ATTN8, "cache_write", "cache_amax", "cache_quant", "fill_u32", CALIB):
         if key in name:
-            if key == ATTN:
-                i = name.find("ILi")
-                return ATTN + (name[i:name.find("EEEv")] if i >= 0 else "")
+            if key in (ATTN, ATTN8):
+                i = name.find(key + "<")
+                return name[i:name.find(">", i) + 1] if i >= 0 else key
             return key
     return name[:60]
 
 
-def stats_md(dirname: str, cmd: str) -> str:
+def steady_attention(dirname: str, steady: int):
+    """(kernel, mean us, calls) of the last `steady` attention dispatches in the
+    kernel trace: the timed steady-state calls of a bench run."""
+    path = _one(dirname, "*kernel_trace.csv")
+    rows = [r for r in csv.DictReader(open(path))
+            if ATTN in r["Kernel_Name"] or ATTN8 in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    last = rows[-steady:]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in last]
+    return short_name(last[-1]["Kernel_Name"]), statistics.mean(durs), len(durs)
+
+
+def stats_md(dirname: str, cmd: str, steady: int = 0) -> str:
     path = _one(dirname, "*kernel_stats.csv")
     rows = list(csv.DictReader(open(path)))
     out = ["# rocprofv3 kernel statistics", "", "Command (from the repository root):", "",
@@ -58,6 +71,10 @@ def stats_md(dirname: str, cmd: str) -> str:
                    f"{ns('AverageNs'):.2f} | {ns('MinNs'):.2f} | {ns('MaxNs'):.2f} | "
                    f"{float(r['Percentage']):.2f} |")
     out.append("")
+    if steady:
+        k, mean_us, n = steady_attention(dirname, steady)
+        out += [f"Steady state (the last {n} calls of {k}, the bench's timed steps, from the "
+                f"kernel trace): mean {mean_us:.2f} us per call.", ""]
     return "\n".join(out)
 
 
@@ -99,6 +116,8 @@ def main(argv=None):
     a.add_argument("dir")
     a.add_argument("--cmd", required=True)
     a.add_argument("--out", required=True)
+    a.add_argument("--steady", type=int, default=0,
+                   help="also report the mean of the last N attention dispatches")
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -111,7 +130,7 @@ def main(argv=None):
     b.add_argument("--md", required=True)
     args = ap.parse_args(argv)
     if args.what == "stats":
-        open(args.out, "w").write(stats_md(args.dir, args.cmd))
+        open(args.out, "w").write(stats_md(args.dir, args.cmd, args.steady))
         return 0
     res, total = traffic(args.fetch, args.write, args.calib_mib, args.steady)
     sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
