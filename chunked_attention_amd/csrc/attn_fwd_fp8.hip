@@ -93,13 +93,22 @@ void attn_fwd_fp8(const AttnArgs a) {
   using G = Geo8<D>;
   constexpr int kKS = G::kKS;
   constexpr int kDB = G::kDB;
-  constexpr int kK0 = 0, kK1 = 1, kV0 = 2, kV1 = 3;
+  // LDS: rings of four K slots and four Vt slots (one 64-key tile each), as
+  // eight separate arrays so that the compiler can tell reads of one slot
+  // from copies landing in another.
   __shared__ __attribute__((aligned(1024))) unsigned char kb0[G::kKBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char kb1[G::kKBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb2[G::kKBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char kb3[G::kKBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vb0[G::kVBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char vb1[G::kVBytes];
-  auto buf = [&](int b) -> unsigned char* {
-    return b == kK0 ? kb0 : b == kK1 ? kb1 : b == kV0 ? vb0 : vb1;
+  __shared__ __attribute__((aligned(1024))) unsigned char vb2[G::kVBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char vb3[G::kVBytes];
+  auto kslot = [&](int b) -> unsigned char* {
+    return b == 0 ? kb0 : b == 1 ? kb1 : b == 2 ? kb2 : kb3;
+  };
+  auto vslot = [&](int b) -> unsigned char* {
+    return b == 0 ? vb0 : b == 1 ? vb1 : b == 2 ? vb2 : vb3;
   };
   __shared__ unsigned s_ticket;
   __shared__ int s_vote[kWaves][2];
@@ -136,7 +145,7 @@ void attn_fwd_fp8(const AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < G::kKInstr; ++u) {
       const int blk = wave * G::kKInstr + u;
-      dma16(c.rk, buf(DST) + blk * 1024, koff[u], sbase + blk * 1024);
+      dma16(c.rk, kslot(DST) + blk * 1024, koff[u], sbase + blk * 1024);
     }
   };
   auto dma_v = [&](auto dst_tag, const TileCursor& c) {
@@ -146,7 +155,7 @@ void attn_fwd_fp8(const AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < G::kVInstr; ++u) {
       const int blk = wave * G::kVInstr + u;
-      dma16(c.rv, buf(DST) + blk * 1024, voff,
+      dma16(c.rv, vslot(DST) + blk * 1024, voff,
             static_cast<uint32_t>(blk) * 16 * pitch + static_cast<uint32_t>(c.k0));
     }
   };
@@ -266,24 +275,36 @@ void attn_fwd_fp8(const AttnArgs a) {
       f32x16_t sacc[2];
       int pf[2][4];   // E4M3 P of the two half tiles: byte (i%4) of word i/4
 
-      TileCursor cj, cv, ck;
-      cursor_seek<D, 1, kBk>(a, cj, t0, h);
-      cv = cj;
-      cursor_next<D, 1, kBk>(a, cv, tlast, h);
-      ck = cv;
-      cursor_next<D, 1, kBk>(a, ck, tlast, h);
       // softmax multiplier of the tile whose scores are being consumed
       auto ceff = [&](const TileCursor& c) { return cq * a.seg[c.s].ks[h]; };
 
+      // ---- prologue.  Ring slots are indexed by (tile - t0) mod 4.  Copy
+      // K of tiles t0..t0+2 and Vt of tiles t0, t0+1 in the order K0 V0 K1
+      // V1 K2, so that from the first tile on the two most recent copy
+      // groups are always those of the current tile (cursors stop at the
+      // piece's last tile, so every copy happens and the vmcnt counts stay
+      // exact); wait for K0, V0, K1 and take the scores of the first half
+      // tile, whose max is the reference.
+      TileCursor cj, cv, ck;
+      cursor_seek<D, 1, kBk>(a, cj, t0, h);
       __syncthreads();
-      dma_k(std::integral_constant<int, kK0>{}, cj);
-      dma_v(std::integral_constant<int, kV0>{}, cj);
-      dma_k(std::integral_constant<int, kK1>{}, cv);
-      wait_dma();
+      ck = cj;
+      cv = cj;
+      dma_k(std::integral_constant<int, 0>{}, ck);
+      dma_v(std::integral_constant<int, 0>{}, cv);
+      cursor_next<D, 1, kBk>(a, ck, tlast, h);
+      cursor_next<D, 1, kBk>(a, cv, tlast, h);
+      dma_k(std::integral_constant<int, 1>{}, ck);
+      dma_v(std::integral_constant<int, 1>{}, cv);
+      cursor_next<D, 1, kBk>(a, ck, tlast, h);
+      cursor_next<D, 1, kBk>(a, cv, tlast, h);      // tile t0+2: next Vt copy
+      dma_k(std::integral_constant<int, 2>{}, ck);
+      cursor_next<D, 1, kBk>(a, ck, tlast, h);      // tile t0+3: next K copy
+      wait_vm_keep_lds_done<G::kVInstr + G::kKInstr>();
       __syncthreads();
       {
         i32x8_t kops[kKS];
-        read_kops(buf(kK0), 0, kops);
+        read_kops(kslot(0), 0, kops);
         qk(kops, q8, q8lo, sacc[0]);
       }
       if (pass == 0) {
@@ -292,25 +313,21 @@ void attn_fwd_fp8(const AttnArgs a) {
         m_ref = raw_max(first) * ceff(cj);
       }
 
-      auto half_step = [&](auto u_tag) {
+      // ---- one tile j (U = (j - t0) mod 4): copy K of tile j+3 (into the
+      // slot tile j-1 used) and Vt of tile j+2 (slot of tile j-2).  Half 0:
+      // softmax of keys 0..31 while computing the scores of keys 32..63 (K
+      // of tile j); half 1: softmax of keys 32..63 while computing the scores
+      // of the next tile's keys 0..31 (K of tile j+1); then P V of the tile.
+      // One wait and one barrier per tile.
+      auto half_tile = [&](auto u_tag, auto hh_tag) {
         constexpr int U = decltype(u_tag)::value;
-        constexpr int HH = U & 1;
-        constexpr int TP = (U >> 1) & 1;
-        constexpr int CUR = U & 1;
-        constexpr int KJ = TP == 0 ? kK0 : kK1;
-        constexpr int KN = TP == 0 ? kK1 : kK0;
-        constexpr int VJ = TP == 0 ? kV0 : kV1;
-        constexpr int VN = TP == 0 ? kV1 : kV0;
-        if (HH == 0) {
-          dma_v(std::integral_constant<int, VN>{}, cv);   // V_{j+1}; V_{j-1} is done
-        } else {
-          dma_k(std::integral_constant<int, KJ>{}, ck);   // K_{j+2}; K_j is done
-        }
+        constexpr int HH = decltype(hh_tag)::value;
+        constexpr int CUR = HH;
         i32x8_t kops[kKS];
         if (HH == 0) {
-          read_kops(buf(KJ), 1, kops);
+          read_kops(kslot(U), 1, kops);
         } else {
-          read_kops(buf(KN), 0, kops);
+          read_kops(kslot((U + 1) & 3), 0, kops);
         }
 
         f32x16_t& sc = sacc[CUR];
@@ -329,61 +346,61 @@ void attn_fwd_fp8(const AttnArgs a) {
           const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[4 * v + 3], c_eff, neg_m));
           pf[HH][v] = pack8<true>(p2, p3, pack8<false>(p0, p1, 0));
         }
-
-        if (HH == 1) {
-          // this tile's values: rescale O if the tile starts a segment with
-          // another V scale, then O^T += Vt . P^T and l += 1 . P^T
-          if (cj.s != pv_seg) {
-            const float vs_new = a.seg[cj.s].vs[h];
-            if (pv_seg >= 0) {
-              const float f = vs_cur / vs_new;
+      };
+      auto tile = [&](auto u_tag) {
+        constexpr int U = decltype(u_tag)::value;
+        dma_k(std::integral_constant<int, (U + 3) & 3>{}, ck);
+        dma_v(std::integral_constant<int, (U + 2) & 3>{}, cv);
+        half_tile(u_tag, std::integral_constant<int, 0>{});
+        half_tile(u_tag, std::integral_constant<int, 1>{});
+        // this tile's values: rescale O if the tile starts a segment with
+        // another V scale, then O^T += Vt . P^T and l += 1 . P^T
+        if (cj.s != pv_seg) {
+          const float vs_new = a.seg[cj.s].vs[h];
+          if (pv_seg >= 0) {
+            const float f = vs_cur / vs_new;
 #pragma unroll
-              for (int db = 0; db < kDB; ++db)
+            for (int db = 0; db < kDB; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= f;
-            }
-            vs_cur = vs_new;
-            pv_seg = cj.s;
+              for (int i = 0; i < 16; ++i) oacc[db][i] *= f;
           }
-          i32x8_t pb;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            pb[v] = pf[0][v];
-            pb[4 + v] = pf[1][v];
-          }
-          const unsigned char* vt = buf(VJ);
-#pragma unroll
-          for (int db = 0; db < kDB; ++db) {
-            const int rr = db * 32 + col;
-            const i32x8_t vops = ld32(vt + swz_off<64>(rr, half * 2), vt + swz_off<64>(rr, half * 2 + 1));
-            oacc[db] = mfma8(vops, pb, oacc[db]);
-          }
-          lacc = mfma8(ones, pb, lacc);
+          vs_cur = vs_new;
+          pv_seg = cj.s;
         }
-        if (HH == 0) {
-          wait_vm_keep_lds_done<G::kVInstr>();
-        } else {
-          wait_vm_keep_lds_done<G::kKInstr>();
+        i32x8_t pb;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          pb[v] = pf[0][v];
+          pb[4 + v] = pf[1][v];
         }
+        const unsigned char* vt = vslot(U);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int rr = db * 32 + col;
+          const i32x8_t vops = ld32(vt + swz_off<64>(rr, half * 2), vt + swz_off<64>(rr, half * 2 + 1));
+          oacc[db] = mfma8(vops, pb, oacc[db]);
+        }
+        lacc = mfma8(ones, pb, lacc);
+        // the next tile reads K of tile j+2 and Vt of tile j+1 (copied one
+        // tile ago: only this tile's copies may stay in flight), and this
+        // wave's LDS reads must be done before any wave refills a slot
+        wait_vm_keep_lds_done<G::kKInstr + G::kVInstr>();
         barrier_no_fence();
-        if (HH == 1) {
-          cursor_next<D, 1, kBk>(a, cj, tlast, h);
-          cursor_next<D, 1, kBk>(a, cv, tlast, h);
-          cursor_next<D, 1, kBk>(a, ck, tlast, h);
-        }
+        cursor_next<D, 1, kBk>(a, cj, tlast, h);
+        cursor_next<D, 1, kBk>(a, cv, tlast, h);
+        cursor_next<D, 1, kBk>(a, ck, tlast, h);
       };
 
       int j = t0;
-      for (; j + 1 < t1; j += 2) {
-        half_step(std::integral_constant<int, 0>{});
-        half_step(std::integral_constant<int, 1>{});
-        half_step(std::integral_constant<int, 2>{});
-        half_step(std::integral_constant<int, 3>{});
+      for (; j + 3 < t1; j += 4) {
+        tile(std::integral_constant<int, 0>{});
+        tile(std::integral_constant<int, 1>{});
+        tile(std::integral_constant<int, 2>{});
+        tile(std::integral_constant<int, 3>{});
       }
-      if (j < t1) {
-        half_step(std::integral_constant<int, 0>{});
-        half_step(std::integral_constant<int, 1>{});
-      }
+      if (j < t1) tile(std::integral_constant<int, 0>{});
+      if (j + 1 < t1) tile(std::integral_constant<int, 1>{});
+      if (j + 2 < t1) tile(std::integral_constant<int, 2>{});
       wait_dma();
       if (pass + 1 >= kMaxPasses) break;
       // a logit more than 2^8 above the reference would saturate E4M3 P:
