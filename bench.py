@@ -116,7 +116,6 @@ def run_stream_bench(w, args, device, flat: bool):
     import gc
     import torch
     import chunked_attention_amd as kv
-    from oracle.attention import kv_length
 
     pool = min(args.pool, w.chunks) if args.pool else w.chunks
     inp = Inputs(w, pool, args.dist, device)
@@ -129,6 +128,9 @@ def run_stream_bench(w, args, device, flat: bool):
         return rs
 
     rings = new_rings()
+    # flat mode: the timed stream runs on a second set of rings made now, so
+    # that nothing is allocated between the warm-up and the timed region
+    fresh = new_rings() if flat else None
     outs = [torch.empty_like(inp.q[0][0]) for _ in range(2)]
     stream = torch.cuda.current_stream()
 
@@ -140,6 +142,7 @@ def run_stream_bench(w, args, device, flat: bool):
     pool_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * per_step + 2)]
     ev_iter = iter(pool_ev)
     attn_events, write_events, step_events = [], [], []
+    kv_len = [0]        # keys attended by the timed calls (largest)
 
     def chunk(t: int, timed: bool):
         c = t % pool
@@ -156,6 +159,8 @@ def run_stream_bench(w, args, device, flat: bool):
                     e1.record(stream)
                     r.attention(inp.q[c][st], out=outs[li & 1])
                     e2.record(stream)
+                    if li == 0:
+                        kv_len[0] = max(kv_len[0], r.info().kv_len)
                     write_events.append((e0, e1))
                     attn_events.append((e1, e2))
                 else:
@@ -185,34 +190,37 @@ def run_stream_bench(w, args, device, flat: bool):
             torch.cuda.synchronize()
         return t
 
-    t = 0
-    if flat:
-        # warm the GPU up on a throwaway stream, then start over from chunk 0
-        t = clock_warmup(t)
-        for _ in range(warmup):
-            chunk(t, False)
-            t += 1
-        torch.cuda.synchronize()
-        rings = new_rings()
-        t = 0
-    else:
-        # fill the window (untimed) so every timed step is a steady-state chunk
-        while t <= w.window:
-            chunk(t, False)
-            t += 1
-        t = clock_warmup(t)
-        for _ in range(warmup):
-            chunk(t, False)
-            t += 1
-    torch.cuda.synchronize()
-    t_first = t
-    start, end = next(ev_iter), next(ev_iter)
-    # the timed region is host-driven: keep Python's collector from pausing
-    # the launches (the GPU would idle behind it)
+    # rocm-smi runs for about a second with the GPU idle, which lets the
+    # clock fall back: read it before the warm-up, never between the warm-up
+    # and the timed region
     tele_before = gpu_telemetry() if flat else None
+    start, end = next(ev_iter), next(ev_iter)
+    # Keep Python's collector from pausing the host-driven launches (the GPU
+    # would idle behind it and lower its clock): collect once now, before the
+    # warm-up, and keep the GPU busy from the warm-up to the timed region.
     gc.collect()
     gc.disable()
     try:
+        t = 0
+        if flat:
+            # warm the GPU up on a throwaway stream, then start over from chunk 0
+            t = clock_warmup(t)
+            for _ in range(warmup):
+                chunk(t, False)
+                t += 1
+            rings = fresh
+            t = 0
+        else:
+            # fill the window (untimed) so every timed step is a steady-state chunk
+            while t <= w.window:
+                chunk(t, False)
+                t += 1
+            t = clock_warmup(t)
+            for _ in range(warmup):
+                chunk(t, False)
+                t += 1
+        torch.cuda.synchronize()
+        t_first = t
         start.record(stream)
         for _ in range(steps):
             chunk(t, True)
@@ -232,13 +240,12 @@ def run_stream_bench(w, args, device, flat: bool):
         "attn_ms": [a.elapsed_time(b) for a, b in attn_events],
         "write_ms": [a.elapsed_time(b) for a, b in write_events],
         "step_ms": step_ms,
-        "kv_len": kv_length(max(t_first, w.window + 1), w.cond_tokens, w.chunk_tokens,
-                            w.window),
+        "kv_len": kv_len[0],
         "first_chunk": t_first,
         "last_chunk": t - 1,
         "calls_per_step": w.steps * w.layers,
         "writes_per_step": (w.steps + 1) * w.layers,
-        "telemetry": {"before": tele_before, "after": tele_after} if flat else None,
+        "telemetry": {"before_warmup": tele_before, "after": tele_after} if flat else None,
     }
     if args.copy_calib_mib:
         # a plain device copy of known size, for scaling the HBM byte counters
@@ -422,7 +429,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": f"attn_fwd_bf16<{w.head_dim},1,false>" if not fp8 else
+            "kernel": f"attn_fwd_bf16<{w.head_dim},false>" if not fp8 else
                       f"attn_fwd_fp8<{w.head_dim},false>",
             "per_launch_flops": flops,
         },

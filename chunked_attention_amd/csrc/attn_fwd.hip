@@ -34,10 +34,9 @@
 //
 // Software pipeline over steps of 32 keys, with K and Vt in rings of four
 // LDS slots each: while the softmax of step s runs on the VALU, the QK^T
-// MFMAs of step s+1 are issued, then the PV MFMAs of step s.  Steps go in
-// pairs: a pair copies the K and Vt two to three steps ahead into the slots
-// the previous pair read, so every copy has two steps to land, and ends
-// with one wait and one barrier.
+// MFMAs of step s+1 are issued, then the PV MFMAs of step s.  K copies run
+// four steps ahead and Vt copies three, so every copy has two steps to land;
+// one barrier per step.
 //
 // Softmax in base 2 with a fixed reference per row piece: t = s*scale*log2(e)
 // and p = 2^(t - m_ref), where m_ref is the max of the piece's first 32 keys,
@@ -227,26 +226,28 @@ void attn_fwd_bf16(const AttnArgs a) {
       f32x16_t sacc[2];   // scores of a step, double-buffered
 
       // ---- prologue.  Ring slots are indexed by (step - t0) mod 4.  Copy
-      // K of steps t0..t0+2 and Vt of steps t0, t0+1 (cursors stop at the
-      // piece's last step, so every slot copy happens and the vmcnt counts
-      // stay exact), wait for them, and take the scores of step t0, whose
-      // max is the reference.
+      // K of steps t0..t0+3 and Vt of steps t0..t0+2 (in the order K0 V0 K1
+      // V1 K2 V2 K3; cursors stop at the piece's last step, so every slot
+      // copy happens and the vmcnt counts stay exact), wait for K0, V0, K1,
+      // and take the scores of step t0, whose max is the reference.
       TileCursor cj, cv, ck;
       cursor_seek<D, 2, kStep>(a, cj, t0, h);
       __syncthreads();
       ck = cj;
-      cv = cj;
       dma_k(std::integral_constant<int, 0>{}, ck);
-      dma_v(std::integral_constant<int, 0>{}, cv);
+      dma_v(std::integral_constant<int, 0>{}, ck);
       cursor_next<D, 2, kStep>(a, ck, tlast, h);
-      cursor_next<D, 2, kStep>(a, cv, tlast, h);
       dma_k(std::integral_constant<int, 1>{}, ck);
-      dma_v(std::integral_constant<int, 1>{}, cv);
+      dma_v(std::integral_constant<int, 1>{}, ck);
       cursor_next<D, 2, kStep>(a, ck, tlast, h);
-      cursor_next<D, 2, kStep>(a, cv, tlast, h);      // step t0+2: next Vt copy
       dma_k(std::integral_constant<int, 2>{}, ck);
-      cursor_next<D, 2, kStep>(a, ck, tlast, h);      // step t0+3: next K copy
-      wait_dma();
+      dma_v(std::integral_constant<int, 2>{}, ck);
+      cv = ck;
+      cursor_next<D, 2, kStep>(a, cv, tlast, h);      // step t0+3: next V copy
+      cursor_next<D, 2, kStep>(a, ck, tlast, h);
+      dma_k(std::integral_constant<int, 3>{}, ck);
+      cursor_next<D, 2, kStep>(a, ck, tlast, h);      // step t0+4: next K copy
+      wait_vm_keep_lds_done<4 * G::kKInstr>();
       __syncthreads();
       {
         bf16x8_t kops[kDS];
@@ -258,31 +259,20 @@ void attn_fwd_bf16(const AttnArgs a) {
         mask(first, cj.rows - cj.k0);
         m_ref = step_max(first);
       }
-      // slot 0 of K is refilled by the first pair of steps: every wave's
-      // reads of it must be done
-      wait_vm_keep_lds_done<0>();
+      // slot 0 of K is refilled by the first step: every wave's reads of it
+      // must be done
+      wait_vm_keep_lds_done<4 * G::kKInstr>();
       barrier_no_fence();
 
-      // ---- steps go in pairs (s, s+1), s - t0 even; a pair copies K of
-      // steps s+3, s+4 and Vt of steps s+2, s+3 into the slots the previous
-      // pair read, reads K of s+1, s+2 and Vt of s, s+1, and ends with one
-      // wait for its own copies and one barrier.
-      auto copies = [&](auto u_tag) {
-        constexpr int U = decltype(u_tag)::value;     // (s - t0) mod 4, even
-        dma_k(std::integral_constant<int, (U + 3) & 3>{}, ck);
-        cursor_next<D, 2, kStep>(a, ck, tlast, h);
-        dma_k(std::integral_constant<int, U>{}, ck);
-        cursor_next<D, 2, kStep>(a, ck, tlast, h);
-        dma_v(std::integral_constant<int, (U + 2) & 3>{}, cv);
-        cursor_next<D, 2, kStep>(a, cv, tlast, h);
-        dma_v(std::integral_constant<int, (U + 3) & 3>{}, cv);
-        cursor_next<D, 2, kStep>(a, cv, tlast, h);
-      };
-      // one step s: scores of step s+1 (K in slot U+1) while running the
-      // softmax of step s, then P V with Vt in slot U
+      // ---- one pipelined step s (U = (s - t0) mod 4): copy K of step s+4
+      // (into the slot step s used) and Vt of step s+3 (into the slot step
+      // s-1 used); read K of step s+1 and Vt of step s; compute the scores
+      // of step s+1 while running the softmax of step s, then add P V.
       auto step = [&](auto u_tag) {
         constexpr int U = decltype(u_tag)::value;
         constexpr int CUR = U & 1;
+        dma_k(std::integral_constant<int, U>{}, ck);
+        dma_v(std::integral_constant<int, (U + 3) & 3>{}, cv);
         bf16x8_t kops[kDS];
         read_kops(kslot((U + 1) & 3), kops);
         bf16x8_t vops[2][kDB];
@@ -340,37 +330,27 @@ void attn_fwd_bf16(const AttnArgs a) {
           for (int db = 0; db < kDB; ++db)
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vops[pp][db], pb[pp], oacc[db],
                                                               0, 0, 0);
-        cursor_next<D, 2, kStep>(a, cj, tlast, h);
-      };
-      // the next pair reads what this pair copied, and this wave's LDS
-      // reads must be done before any wave refills a slot
-      auto pair_end = [&]() {
-        wait_vm_keep_lds_done<0>();
+        // the next step reads K of step s+2 and Vt of step s+1 (copied two
+        // steps ago: only the last two steps' copies may stay in flight),
+        // and this wave's LDS reads must be done before any wave refills a
+        // slot
+        wait_vm_keep_lds_done<2 * (G::kKInstr + G::kVInstr)>();
         barrier_no_fence();
+        cursor_next<D, 2, kStep>(a, cj, tlast, h);
+        cursor_next<D, 2, kStep>(a, cv, tlast, h);
+        cursor_next<D, 2, kStep>(a, ck, tlast, h);
       };
 
       int j = t0;
       for (; j + 3 < t1; j += 4) {
-        copies(std::integral_constant<int, 0>{});
         step(std::integral_constant<int, 0>{});
         step(std::integral_constant<int, 1>{});
-        pair_end();
-        copies(std::integral_constant<int, 2>{});
         step(std::integral_constant<int, 2>{});
         step(std::integral_constant<int, 3>{});
-        pair_end();
       }
-      if (j < t1) {
-        copies(std::integral_constant<int, 0>{});
-        step(std::integral_constant<int, 0>{});
-        if (j + 1 < t1) step(std::integral_constant<int, 1>{});
-        pair_end();
-        if (j + 2 < t1) {
-          copies(std::integral_constant<int, 2>{});
-          step(std::integral_constant<int, 2>{});
-          pair_end();
-        }
-      }
+      if (j < t1) step(std::integral_constant<int, 0>{});
+      if (j + 1 < t1) step(std::integral_constant<int, 1>{});
+      if (j + 2 < t1) step(std::integral_constant<int, 2>{});
       // no copy may still land in a slot the next pass or piece refills
       wait_dma();
 
