@@ -308,3 +308,77 @@ def test_golden_visible_sets():
         assert O1.kv_length(t, m, n, W) == S, line
         rows += 1
     assert rows >= 15
+
+
+# --------------------------------------------------------------------------
+# token groups: reference tokens R (always visible) and the chunk's source
+# tokens S_t (queried with the chunk, visible to it only).  O1's explicit
+# assembly against O2's label mask catches a source segment leaking into the
+# history, R placed after the sink but dropped for chunk 0, source queries
+# seeing a different set than the chunk's own queries.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window", [0, 1, 2, 4])
+@pytest.mark.parametrize("m,r,s", [(0, 3, 0), (4, 0, 5), (4, 3, 5), (0, 0, 2)])
+def test_o1_equals_brute_force_with_token_groups(window, m, r, s):
+    rng = np.random.default_rng(1000 + 100 * window + 10 * r + s + m)
+    T, n, H, d = 6, 5, 2, 8
+    scale = 1 / math.sqrt(d)
+    qs = [rnd(rng, n + s, H, d) for _ in range(T)]
+    ks = [rnd(rng, n + s, H, d) for _ in range(T)]
+    vs = [rnd(rng, n + s, H, d) for _ in range(T)]
+    ck = rnd(rng, m, H, d) if m else None
+    cv = rnd(rng, m, H, d) if m else None
+    rk = rnd(rng, r, H, d) if r else None
+    rv = rnd(rng, r, H, d) if r else None
+    ref = O2.group_stream_attention(qs, ks, vs, ck, cv, rk, rv, n, window, scale)
+    so = O1.StreamOracle(window, scale, ck, cv, rk, rv)
+    for t in range(T):
+        src_k = ks[t][n:] if s else None
+        src_v = vs[t][n:] if s else None
+        o, _ = so.attend(t, qs[t], ks[t][:n], vs[t][:n], src_k=src_k, src_v=src_v)
+        so.commit(t, ks[t][:n], vs[t][:n])
+        np.testing.assert_allclose(o, ref[t], rtol=0, atol=1e-12)
+
+
+def test_group_mask_without_groups_is_the_plain_stream_mask():
+    # with no reference and no source tokens the label mask is the chunk mask
+    m, n, T, W = 3, 4, 8, 2
+    kg, kc = O2.group_labels(m, 0, n, 0, T)
+    qc = np.repeat(np.arange(T), n)
+    np.testing.assert_array_equal(O2.group_mask(kg, kc, qc, W), O2.stream_mask(m, n, T, W))
+
+
+def test_group_mask_counts_match_closed_form():
+    # every query of chunk t (target or source) sees |S(t)| =
+    # m + r + n * (visible chunks + 1) + s keys, and never another chunk's
+    # source tokens
+    m, r, n, s, T, W = 2, 3, 4, 5, 9, 2
+    kg, kc = O2.group_labels(m, r, n, s, T)
+    qc = np.repeat(np.arange(T), n + s)
+    mask = O2.group_mask(kg, kc, qc, W)
+    for t in range(T):
+        for row in (t * (n + s), t * (n + s) + n + s - 1):
+            assert mask[row].sum() == O1.kv_length(t, m, n, W, r, s)
+            src_seen = (kg == O2.SOURCE) & mask[row]
+            assert set(kc[src_seen]) <= {t}
+    # hand count, 720p-shaped groups (m=256, R = S = one latent frame of
+    # 1620 tokens, W=3, steady): cond 256 + ref 1620 + sink, 3 window chunks
+    # and the current chunk 5 * 1620 + source 1620 = 11596 keys
+    assert O1.kv_length(4, 256, 1620, 3, 1620, 1620) == 11596
+
+
+def test_source_queries_see_the_same_keys_as_the_chunk():
+    # a source-token query and a chunk-token query with the same vector get the
+    # same output: both attend the same set
+    rng = np.random.default_rng(3)
+    n, s, H, d = 4, 3, 1, 8
+    ck, cv = rnd(rng, 2, H, d), rnd(rng, 2, H, d)
+    hk, hv = [rnd(rng, n, H, d)], [rnd(rng, n, H, d)]
+    cur_k, cur_v = rnd(rng, n, H, d), rnd(rng, n, H, d)
+    src_k, src_v = rnd(rng, s, H, d), rnd(rng, s, H, d)
+    q = rnd(rng, n + s, H, d)
+    q[n + 1] = q[2]
+    o, lse = O1.chunk_attention(q, ck, cv, hk, hv, cur_k, cur_v, 0.5, src_k=src_k, src_v=src_v)
+    np.testing.assert_array_equal(o[n + 1], o[2])
+    np.testing.assert_array_equal(lse[:, n + 1], lse[:, 2])
