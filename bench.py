@@ -31,7 +31,8 @@ PEAK_HBM_GBPS = 8000.0
 
 
 def attn_flops(w, kv_len: int) -> float:
-    return 4.0 * w.chunk_tokens * kv_len * w.head_dim * w.heads
+    """QK^T + PV of one call: the chunk's own and source queries over kv_len keys."""
+    return 4.0 * (w.chunk_tokens + w.source_tokens) * kv_len * w.head_dim * w.heads
 
 
 def cpu_baseline(w, seconds: float, seed_dist: str = "baseline") -> dict:
@@ -45,27 +46,32 @@ def cpu_baseline(w, seconds: float, seed_dist: str = "baseline") -> dict:
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    import torch
     s = synth.Stream(w, seed_dist)
     t = w.window + 1
     ids = O1.visible_chunks(t, w.window)
-    ck, cv = s.kv_cond()
+    f64 = O1.as_f64
+    ck, cv = (f64(x) for x in s.kv_cond()) if w.cond_tokens else (None, None)
+    rk, rv = (f64(x) for x in s.kv_ref()) if w.ref_tokens else (None, None)
+    sk, sv = (f64(x) for x in s.kv_src(t)) if w.source_tokens else (None, None)
     hist = [s.kv_clean(j) for j in ids]
     k, v = s.kv_noisy(t)
-    q = s.q(t)
-    f64 = O1.as_f64
-    args = (f64(q), f64(ck), f64(cv), [f64(a) for a, _ in hist], [f64(b) for _, b in hist],
+    q = torch.cat([s.q(t), s.q_src(t)]) if w.source_tokens else s.q(t)
+    args = (f64(q), ck, cv, [f64(a) for a, _ in hist], [f64(b) for _, b in hist],
             f64(k), f64(v), w.scale)
+    kw = dict(ref_k=rk, ref_v=rv, src_k=sk, src_v=sv)
 
     t0 = time.perf_counter()
-    O1.chunk_attention(*args)
+    O1.chunk_attention(*args, **kw)
     one = time.perf_counter() - t0
     reps = max(1, int(round(seconds / max(one, 1e-3))))
     t0 = time.perf_counter()
     for _ in range(reps - 1):
-        O1.chunk_attention(*args)
+        O1.chunk_attention(*args, **kw)
     dt = one + time.perf_counter() - t0
-    kv_len = O1.kv_length(t, w.cond_tokens, w.chunk_tokens, w.window)
-    flops = 4.0 * w.chunk_tokens * kv_len * w.head_dim * w.heads * reps
+    kv_len = O1.kv_length(t, w.cond_tokens, w.chunk_tokens, w.window, w.ref_tokens,
+                          w.source_tokens)
+    flops = attn_flops(w, kv_len) * reps
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -95,15 +101,31 @@ class Inputs:
     """Per-chunk inputs uploaded once (a pool of `pool` chunk sets)."""
 
     def __init__(self, w, pool: int, dist: str, device):
+        import torch
         import synth
         s = synth.Stream(w, dist)
+        src = w.source_tokens > 0
+
+        def up(own, extra=None):
+            # with source tokens a chunk's rows are its own tokens, then its
+            # source tokens (queries, staged and committed K/V alike)
+            return (torch.cat([own, extra]) if src else own).to(device)
+
         self.cond = tuple(x.to(device) for x in s.kv_cond()) if w.cond_tokens else None
+        self.ref = tuple(x.to(device) for x in s.kv_ref()) if w.ref_tokens else None
         self.q, self.noisy, self.clean = [], [], []
         for c in range(pool):
-            self.q.append([s.q(c, st).to(device) for st in range(w.steps)])
-            self.noisy.append([tuple(x.to(device) for x in s.kv_noisy(c, st))
-                               for st in range(w.steps)])
-            self.clean.append(tuple(x.to(device) for x in s.kv_clean(c)))
+            qs, noisy = [], []
+            for st in range(w.steps):
+                k, v = s.kv_noisy(c, st)
+                sk, sv = s.kv_src(c, st) if src else (None, None)
+                qs.append(up(s.q(c, st), s.q_src(c, st) if src else None))
+                noisy.append((up(k, sk), up(v, sv)))
+            k, v = s.kv_clean(c)
+            sk, sv = s.kv_src_clean(c) if src else (None, None)
+            self.q.append(qs)
+            self.noisy.append(noisy)
+            self.clean.append((up(k, sk), up(v, sv)))
         self.pool = pool
 
 
@@ -121,10 +143,13 @@ def run_stream_bench(w, args, device, flat: bool):
     inp = Inputs(w, pool, args.dist, device)
     def new_rings():
         rs = [kv.Ring(w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window,
-                      kv_dtype=w.kv_dtype, device=device) for _ in range(w.layers)]
-        if inp.cond:
-            for r in rs:
+                      kv_dtype=w.kv_dtype, device=device, ref_tokens=w.ref_tokens,
+                      source_tokens=w.source_tokens) for _ in range(w.layers)]
+        for r in rs:
+            if inp.cond:
                 r.cond(*inp.cond)
+            if inp.ref:
+                r.ref(*inp.ref)
         return rs
 
     rings = new_rings()
@@ -138,7 +163,7 @@ def run_stream_bench(w, args, device, flat: bool):
         warmup, steps = args.warmup, w.chunks
     else:
         warmup, steps = args.warmup, args.steps
-    per_step = w.steps * w.layers * 3 + w.layers * 2 + 1
+    per_step = w.steps * w.layers * 3 + w.layers * 4 + 1
     pool_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * per_step + 2)]
     ev_iter = iter(pool_ev)
     attn_events, write_events, step_events = [], [], []
@@ -166,15 +191,25 @@ def run_stream_bench(w, args, device, flat: bool):
                 else:
                     r.stage(*inp.noisy[c][st])
                     r.attention(inp.q[c][st], out=outs[li & 1])
-        for r in rings:
+        for li, r in enumerate(rings):
             if timed:
                 e0, e1 = next(ev_iter), next(ev_iter)
                 e0.record(stream)
                 r.commit(*inp.clean[c])
                 e1.record(stream)
                 write_events.append((e0, e1))
+                if args.clean_pass:
+                    # the clean pass: one more attention call per layer over
+                    # the committed chunk (queries of the clean latent; the
+                    # first step's stand in)
+                    e2 = next(ev_iter)
+                    r.attention(inp.q[c][0], out=outs[li & 1])
+                    e2.record(stream)
+                    attn_events.append((e1, e2))
             else:
                 r.commit(*inp.clean[c])
+                if args.clean_pass:
+                    r.attention(inp.q[c][0], out=outs[li & 1])
             r.evict()
 
     def clock_warmup(t: int) -> int:
@@ -243,7 +278,7 @@ def run_stream_bench(w, args, device, flat: bool):
         "kv_len": kv_len[0],
         "first_chunk": t_first,
         "last_chunk": t - 1,
-        "calls_per_step": w.steps * w.layers,
+        "calls_per_step": (w.steps + (1 if args.clean_pass else 0)) * w.layers,
         "writes_per_step": (w.steps + 1) * w.layers,
         "telemetry": {"before_warmup": tele_before, "after": tele_after} if flat else None,
     }
@@ -333,13 +368,16 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--warmup-ms", type=float, default=400.0,
                     help="untimed chunks run first for at least this long (GPU clock ramp)")
-    ap.add_argument("--config", default="720p", choices=["tiny", "720p", "depth", "long", "fp8"])
+    ap.add_argument("--config", default="720p",
+                    choices=["tiny", "720p", "depth", "long", "fp8", "groups", "edit3"])
     ap.add_argument("--dist", default="baseline")
     ap.add_argument("--pool", type=int, default=16, help="distinct input chunks uploaded")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--window", type=int, default=None,
                     help="override the config's window W (e.g. the long stream at W=3)")
+    ap.add_argument("--clean-pass", action="store_true",
+                    help="one more attention call per layer after each COMMIT (clean pass)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -366,6 +404,9 @@ def main() -> int:
         import dataclasses
         w = dataclasses.replace(w, window=args.window, name=f"{w.name}-W{args.window}")
     flat = args.config == "long"
+    if flat and args.clean_pass:
+        print("--clean-pass is not timed per chunk in the long-stream mode", file=sys.stderr)
+        return 2
 
     r = run_stream_bench(w, args, device, flat)
     flops = attn_flops(w, r["kv_len"])
@@ -382,7 +423,8 @@ def main() -> int:
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
     achieved = flops / (attn_us * 1e-6) / 1e12
     e = 1 if fp8 else 2
-    write_bytes = 2 * w.chunk_tokens * w.heads * w.head_dim * (2 + e)   # read bf16 K,V + write
+    # read bf16 K and V, write them in the ring's type
+    write_bytes = 2 * (w.chunk_tokens + w.source_tokens) * w.heads * w.head_dim * (2 + e)
     value = flops * r["calls_per_step"] / step_s / 1e12
     steps_ms = r["step_ms"]
     med = statistics.median(steps_ms)
@@ -404,13 +446,17 @@ def main() -> int:
         "data": "synthetic (seeded N(0, std^2) bf16 chunks, resident in HBM)",
         "config": {
             "workload": f"{w.name}: H={w.heads} d={w.head_dim} n={w.chunk_tokens} "
-                        f"m={w.cond_tokens} W={w.window} layers={w.layers} steps={w.steps}, "
+                        f"m={w.cond_tokens} r={w.ref_tokens} s={w.source_tokens} "
+                        f"W={w.window} layers={w.layers} steps={w.steps}"
+                        f"{' +clean pass' if args.clean_pass else ''}, "
                         f"steady-state chunks {r['first_chunk']}..{r['last_chunk']} "
                         f"(|S|={r['kv_len']} keys); one step = STAGE + attention per "
                         f"denoise step and layer, COMMIT + evict per layer",
             "heads": w.heads, "head_dim": w.head_dim, "chunk_tokens": w.chunk_tokens,
             "cond_tokens": w.cond_tokens, "window": w.window, "kv_len": r["kv_len"],
             "layers": w.layers, "denoise_steps": w.steps, "kv_dtype": w.kv_dtype,
+            "ref_tokens": w.ref_tokens, "source_tokens": w.source_tokens,
+            "clean_pass": args.clean_pass,
         },
         "chunks_per_s": round(1.0 / step_s, 2),
         "pct_mfma_peak": round(100 * value / peak, 2),

@@ -31,10 +31,12 @@ KVC_KV_FP8_E4M3 = 1
 KVC_COND = 0
 KVC_STAGE = 1
 KVC_COMMIT = 2
+KVC_REF = 3
 KVC_PHASE_EMPTY = 0
 KVC_PHASE_STAGED = 1
 KVC_PHASE_COMMITTED = 2
 KVC_MAX_WINDOW = 29
+KVC_MAX_SEGMENTS = KVC_MAX_WINDOW + 5
 KVC_TILE_KEYS = 64
 KVC_ALIGN = 256
 
@@ -45,13 +47,14 @@ class kvc_config(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("chunk_tokens", ctypes.c_int32), ("cond_tokens", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("ref_tokens", ctypes.c_int32),
+                ("source_tokens", ctypes.c_int32)]
 
 
 class kvc_info(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "chunk", "phase", "cond_valid", "sink_valid", "n_window", "kv_len", "n_segments",
-        "free_slots")]
+        "free_slots", "ref_valid")]
 
 
 class kvc_segment(ctypes.Structure):
@@ -137,9 +140,16 @@ def _stream_handle(stream) -> ctypes.c_void_p:
 
 
 def make_config(heads: int, head_dim: int, chunk_tokens: int, cond_tokens: int, window: int,
-                kv_dtype: str = "bf16", softmax_scale: float = 0.0) -> kvc_config:
+                kv_dtype: str = "bf16", softmax_scale: float = 0.0, ref_tokens: int = 0,
+                source_tokens: int = 0) -> kvc_config:
     return kvc_config(heads, head_dim, chunk_tokens, cond_tokens, window, _DTYPES[kv_dtype],
-                      softmax_scale)
+                      softmax_scale, ref_tokens, source_tokens)
+
+
+def query_rows(cfg: kvc_config) -> int:
+    """Rows of q / o / lse of an attention call: the chunk's own tokens
+    followed by its source tokens."""
+    return cfg.chunk_tokens + cfg.source_tokens
 
 
 # ---- the C entry points, over torch tensors --------------------------------
@@ -166,7 +176,7 @@ def _check_tokens(x, rows: int, cfg: kvc_config, what: str) -> None:
 
 
 def kvc_append_chunk(handle, cfg: kvc_config, kind: int, k, v, stream=None) -> None:
-    rows = cfg.cond_tokens if kind == KVC_COND else cfg.chunk_tokens
+    rows = {KVC_COND: cfg.cond_tokens, KVC_REF: cfg.ref_tokens}.get(kind, query_rows(cfg))
     _check_tokens(k, rows, cfg, "k")
     _check_tokens(v, rows, cfg, "v")
     _check(lib().kvc_append_chunk(handle, kind, ctypes.c_void_p(k.data_ptr()),
@@ -176,13 +186,15 @@ def kvc_append_chunk(handle, cfg: kvc_config, kind: int, k, v, stream=None) -> N
 
 def chunk_attn_fwd(handle, cfg: kvc_config, q, o, lse=None, stream=None) -> None:
     import torch
-    _check_tokens(q, cfg.chunk_tokens, cfg, "q")
-    _check_tokens(o, cfg.chunk_tokens, cfg, "o")
+    nq = query_rows(cfg)
+    _check_tokens(q, nq, cfg, "q")
+    _check_tokens(o, nq, cfg, "o")
     lse_ptr = None
     if lse is not None:
         if lse.dtype != torch.float32 or not lse.is_contiguous() or \
-                tuple(lse.shape) != (cfg.heads, cfg.chunk_tokens):
-            raise ValueError("lse must be a contiguous float32 [heads, chunk_tokens] tensor")
+                tuple(lse.shape) != (cfg.heads, nq):
+            raise ValueError("lse must be a contiguous float32 [heads, chunk_tokens + "
+                             "source_tokens] tensor")
         lse_ptr = lse.data_ptr()
     _check(lib().chunk_attn_fwd(handle, ctypes.c_void_p(q.data_ptr()),
                                 ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(lse_ptr),
@@ -206,9 +218,10 @@ def kvc_get_info(handle) -> kvc_info:
 
 
 def kvc_get_segments(handle) -> list[tuple[int, int, int, int]]:
-    buf = (kvc_segment * 32)()
+    buf = (kvc_segment * KVC_MAX_SEGMENTS)()
     count = ctypes.c_int32()
-    _check(lib().kvc_get_segments(handle, buf, 32, ctypes.byref(count)), "kvc_get_segments")
+    _check(lib().kvc_get_segments(handle, buf, KVC_MAX_SEGMENTS, ctypes.byref(count)),
+           "kvc_get_segments")
     return [(s.chunk, s.slot, s.rows, s.role) for s in buf[:count.value]]
 
 
@@ -223,10 +236,10 @@ class Ring:
 
     def __init__(self, heads: int, head_dim: int, chunk_tokens: int, cond_tokens: int,
                  window: int, kv_dtype: str = "bf16", softmax_scale: float = 0.0,
-                 device="cuda"):
+                 device="cuda", ref_tokens: int = 0, source_tokens: int = 0):
         import torch
         self.cfg = make_config(heads, head_dim, chunk_tokens, cond_tokens, window, kv_dtype,
-                               softmax_scale)
+                               softmax_scale, ref_tokens, source_tokens)
         nbytes = kvc_required_bytes(self.cfg)
         if nbytes == 0:
             raise KvcError(KVC_E_INVAL, "kvc_required_bytes")
@@ -246,6 +259,9 @@ class Ring:
 
     def cond(self, k, v, stream=None) -> None:
         kvc_append_chunk(self.handle, self.cfg, KVC_COND, k, v, stream)
+
+    def ref(self, k, v, stream=None) -> None:
+        kvc_append_chunk(self.handle, self.cfg, KVC_REF, k, v, stream)
 
     def stage(self, k, v, stream=None) -> None:
         kvc_append_chunk(self.handle, self.cfg, KVC_STAGE, k, v, stream)

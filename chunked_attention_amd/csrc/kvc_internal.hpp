@@ -11,7 +11,7 @@
 
 namespace kvc {
 
-constexpr int kMaxSegments = KVC_MAX_WINDOW + 3;   // cond + sink + W + current
+constexpr int kMaxSegments = KVC_MAX_SEGMENTS;   // cond, ref, sink, W, current, source
 constexpr int kTileKeys = KVC_TILE_KEYS;
 
 // Attention work decomposition (shared by the launcher and the workspace

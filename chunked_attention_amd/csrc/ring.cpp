@@ -1,8 +1,9 @@
 // Ring-buffer KV cache and the C ABI (host side, plain C++17).
 //
-// The cache holds the condition rows, the global sink (chunk 0), a sliding
-// window of the W most recent committed chunks and one staging slot for the
-// chunk being generated: W + 2 chunk slots recycled in place, so memory and
+// The cache holds the condition rows, the reference rows, the global sink
+// (chunk 0), a sliding window of the W most recent committed chunks, one
+// staging slot for the chunk being generated and one slot for that chunk's
+// source tokens: W + 2 chunk slots recycled in place, so memory and
 // per-chunk work stay bounded for an open-ended stream (discuss.pytorch.kr
 // "JoyAI-Video-Edit 소개", real-time deployment section; ta-paperlens section
 // 5, per-chunk loop: denoise with the cache as history, then update it keeping
@@ -10,6 +11,7 @@
 //
 // Every call validates first, then launches, and only then changes state, so
 // a failed call leaves the ring as it was.
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -26,6 +28,8 @@ bool config_ok(const kvc_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return false;
   if (c->chunk_tokens < 1 || c->chunk_tokens > (1 << 20)) return false;
   if (c->cond_tokens < 0 || c->cond_tokens > (1 << 20)) return false;
+  if (c->ref_tokens < 0 || c->ref_tokens > (1 << 20)) return false;
+  if (c->source_tokens < 0 || c->source_tokens > (1 << 20)) return false;
   if (c->window < 0 || c->window > KVC_MAX_WINDOW) return false;
   if (c->kv_dtype != KVC_KV_BF16 && c->kv_dtype != KVC_KV_FP8_E4M3) return false;
   if (!(c->softmax_scale >= 0.f) || !std::isfinite(c->softmax_scale)) return false;
@@ -51,7 +55,9 @@ SlotGeom make_slot(const kvc_config& c, int rows, size_t offset) {
 
 struct Layout {
   SlotGeom cond;                 // rows == 0 when m == 0
+  SlotGeom ref;                  // rows == 0 when r == 0
   SlotGeom chunk[KVC_MAX_WINDOW + 2];
+  SlotGeom source;               // rows == 0 when s == 0
   int n_slots = 0;
   size_t scratch_off = 0, scratch_bytes = 0;     // cache-write scratch (fp8)
   size_t work_off = 0, work_bytes = 0;           // attention workspace
@@ -65,20 +71,30 @@ Layout make_layout(const kvc_config& c) {
     L.cond = make_slot(c, c.cond_tokens, off);
     off += L.cond.bytes;
   }
+  if (c.ref_tokens > 0) {
+    L.ref = make_slot(c, c.ref_tokens, off);
+    off += L.ref.bytes;
+  }
   L.n_slots = c.window + 2;
   for (int i = 0; i < L.n_slots; ++i) {
     L.chunk[i] = make_slot(c, c.chunk_tokens, off);
     off += L.chunk[i].bytes;
   }
+  if (c.source_tokens > 0) {
+    L.source = make_slot(c, c.source_tokens, off);
+    off += L.source.bytes;
+  }
   if (c.kv_dtype == KVC_KV_FP8_E4M3) {
-    const int maxrows = c.chunk_tokens > c.cond_tokens ? c.chunk_tokens : c.cond_tokens;
+    const int maxrows = std::max(std::max(c.chunk_tokens, c.cond_tokens),
+                                 std::max(c.ref_tokens, c.source_tokens));
     L.scratch_off = off;
     L.scratch_bytes = align_up(sizeof(float) * 2 * c.heads * (pad_rows(maxrows) / kTileKeys),
                                KVC_ALIGN);
     off += L.scratch_bytes;
   }
   L.work_off = off;
-  L.work_bytes = align_up(attention_workspace_bytes(c.heads, c.head_dim, c.chunk_tokens,
+  L.work_bytes = align_up(attention_workspace_bytes(c.heads, c.head_dim,
+                                                    c.chunk_tokens + c.source_tokens,
                                                     c.kv_dtype), KVC_ALIGN);
   off += L.work_bytes;
   L.total = off;
@@ -105,6 +121,7 @@ struct kvc_ring {
   int staging;            // staging slot in phase STAGED, -1 otherwise
   int current;            // slot of the current chunk (STAGED or COMMITTED)
   int cond_valid;
+  int ref_valid;
   int work_ready;         // attention workspace counters initialised
 };
 
@@ -150,16 +167,22 @@ AttnSegment seg_of(const kvc_ring* r, const SlotGeom& g) {
   return s;
 }
 
-// Logical segment table for an attention call now: [cond ; sink ; window
-// chunks max(1,t-W)..t-1 oldest first ; current].  Returns the count, or -1
-// when no call is possible.
+// Logical segment table for an attention call now: [cond ; ref ; sink ;
+// window chunks max(1,t-W)..t-1 oldest first ; current ; source].  Returns
+// the count, or -1 when no call is possible.
 int segment_table(const kvc_ring* r, kvc_segment* info, AttnSegment* dev) {
   if (r->phase == KVC_PHASE_EMPTY) return -1;
   if (r->cfg.cond_tokens > 0 && !r->cond_valid) return -1;
+  if (r->cfg.ref_tokens > 0 && !r->ref_valid) return -1;
   int n = 0;
   if (r->cfg.cond_tokens > 0) {
     if (info) info[n] = kvc_segment{-1, -1, r->cfg.cond_tokens, 0};
     if (dev) dev[n] = seg_of(r, r->L.cond);
+    ++n;
+  }
+  if (r->cfg.ref_tokens > 0) {
+    if (info) info[n] = kvc_segment{-1, -3, r->cfg.ref_tokens, 4};
+    if (dev) dev[n] = seg_of(r, r->L.ref);
     ++n;
   }
   const int t = r->t;
@@ -184,6 +207,11 @@ int segment_table(const kvc_ring* r, kvc_segment* info, AttnSegment* dev) {
   if (info) info[n] = kvc_segment{t, r->current, r->cfg.chunk_tokens, 3};
   if (dev) dev[n] = seg_of(r, r->L.chunk[r->current]);
   ++n;
+  if (r->cfg.source_tokens > 0) {
+    if (info) info[n] = kvc_segment{t, -4, r->cfg.source_tokens, 5};
+    if (dev) dev[n] = seg_of(r, r->L.source);
+    ++n;
+  }
   return n;
 }
 
@@ -222,6 +250,7 @@ kvc_status kvc_create(const kvc_config* cfg, void* dev_buf, size_t bytes, kvc_ri
   r->staging = -1;
   r->current = -1;
   r->cond_valid = 0;
+  r->ref_valid = 0;
   *out = r;
   return KVC_OK;
 }
@@ -236,12 +265,27 @@ kvc_status kvc_append_chunk(kvc_ring* r, int32_t kind, const void* k, const void
     r->cond_valid = 1;
     return KVC_OK;
   }
+  if (kind == KVC_REF) {
+    if (r->cfg.ref_tokens <= 0) return KVC_E_INVAL;
+    kvc_status s = launch_cache_write(write_desc(r, r->L.ref, k, v), stream);
+    if (s != KVC_OK) return s;
+    r->ref_valid = 1;
+    return KVC_OK;
+  }
   if (kind != KVC_STAGE && kind != KVC_COMMIT) return KVC_E_INVAL;
   if (r->phase == KVC_PHASE_COMMITTED) return KVC_E_STATE;
   int slot = r->phase == KVC_PHASE_STAGED ? r->staging : free_slot(r);
   if (slot < 0) return KVC_E_STATE;
   kvc_status s = launch_cache_write(write_desc(r, r->L.chunk[slot], k, v), stream);
   if (s != KVC_OK) return s;
+  if (r->cfg.source_tokens > 0) {
+    // rows n.. of the caller's tensors are the chunk's source tokens
+    const size_t skip = static_cast<size_t>(r->cfg.chunk_tokens) * r->cfg.heads *
+                        r->cfg.head_dim * 2;
+    s = launch_cache_write(write_desc(r, r->L.source, static_cast<const char*>(k) + skip,
+                                      static_cast<const char*>(v) + skip), stream);
+    if (s != KVC_OK) return s;
+  }
   r->current = slot;
   if (kind == KVC_STAGE) {
     r->staging = slot;
@@ -271,7 +315,7 @@ kvc_status chunk_attn_fwd(kvc_ring* r, const void* q, void* o, float* lse, void*
   d.q = q;
   d.o = o;
   d.lse = lse;
-  d.n = r->cfg.chunk_tokens;
+  d.n = r->cfg.chunk_tokens + r->cfg.source_tokens;
   d.heads = r->cfg.heads;
   d.head_dim = r->cfg.head_dim;
   d.kv_dtype = r->cfg.kv_dtype;
@@ -330,6 +374,7 @@ kvc_status kvc_get_info(const kvc_ring* r, kvc_info* out) {
   i.chunk = r->t;
   i.phase = r->phase;
   i.cond_valid = r->cond_valid;
+  i.ref_valid = r->ref_valid;
   i.sink_valid = r->sink_slot >= 0;
   i.n_window = r->n_win;
   kvc_segment segs[kMaxSegments];
@@ -363,6 +408,12 @@ kvc_status kvc_get_slot(const kvc_ring* r, int32_t which, kvc_slot_view* out) {
   } else if (which == -2) {
     if (r->current < 0) return KVC_E_STATE;
     g = &r->L.chunk[r->current];
+  } else if (which == -3) {
+    if (r->cfg.ref_tokens <= 0 || !r->ref_valid) return KVC_E_STATE;
+    g = &r->L.ref;
+  } else if (which == -4) {
+    if (r->cfg.source_tokens <= 0 || r->current < 0) return KVC_E_STATE;
+    g = &r->L.source;
   } else if (which >= 0) {
     for (int s = 0; s < r->L.n_slots; ++s)
       if (r->slot_chunk[s] == which) g = &r->L.chunk[s];

@@ -11,6 +11,17 @@
  * so the attended set, and with it per-chunk cost and memory, stays bounded
  * however long the stream runs.  After a chunk is generated its clean K/V is
  * cached for later chunks; the cache keeps only the sink and the window.
+ *
+ * Two more token groups of the same model are optional: reference tokens R
+ * (an optional reference image's latent tokens, visible to every chunk, like
+ * the condition tokens) and the source tokens S_t of the chunk being edited
+ * (the aligned source-video chunk).  The active chunk sees its own source
+ * tokens bidirectionally; they are queried together with the chunk's own
+ * tokens and are never cached as history.  Source: discuss.pytorch.kr
+ * "JoyAI-Video-Edit 소개", the token-group paragraphs of the architecture
+ * section (noise, global, history, condition, reference and source groups
+ * and the attention mask between them) and of the chunk-wise adaptation
+ * section (visibility of each group from the active chunk).
  * Sources: discuss.pytorch.kr "JoyAI-Video-Edit 소개", sections on the
  * chunk-wise autoregressive adaptation (paper section 4.1) and the real-time
  * deployment pipeline (paper section 5); ta-paperlens "論文解説:
@@ -58,13 +69,15 @@ typedef int32_t kvc_status;
 #define KVC_COND    0   /* condition tokens (m rows) */
 #define KVC_STAGE   1   /* K/V of the current chunk for the present denoise step */
 #define KVC_COMMIT  2   /* clean K/V of the current chunk, kept as history */
+#define KVC_REF     3   /* reference tokens (r rows), always visible */
 
 /* ring phases reported by kvc_get_info */
 #define KVC_PHASE_EMPTY      0   /* no current chunk */
 #define KVC_PHASE_STAGED     1   /* current chunk holds staged (noisy) K/V */
 #define KVC_PHASE_COMMITTED  2   /* current chunk was committed, not yet evicted */
 
-#define KVC_MAX_WINDOW   29       /* W <= 29: at most 32 visible segments */
+#define KVC_MAX_WINDOW   29       /* W <= 29 */
+#define KVC_MAX_SEGMENTS (KVC_MAX_WINDOW + 5)   /* cond, ref, sink, W window, current, source */
 #define KVC_TILE_KEYS    64       /* stored rows are padded to a multiple of this */
 #define KVC_ALIGN        256      /* dev_buf alignment */
 
@@ -76,6 +89,9 @@ typedef struct kvc_config {
   int32_t window;         /* W, 0..KVC_MAX_WINDOW: earlier chunks kept besides the sink */
   int32_t kv_dtype;       /* KVC_KV_BF16 or KVC_KV_FP8_E4M3 */
   float softmax_scale;    /* > 0, or 0 for 1/sqrt(head_dim) */
+  int32_t ref_tokens;     /* r >= 0: reference tokens (keys/values only, always visible) */
+  int32_t source_tokens;  /* s >= 0: source tokens per chunk (queried and attended with the
+                             chunk; never kept as history) */
 } kvc_config;
 
 typedef struct kvc_ring kvc_ring;   /* opaque host handle */
@@ -85,8 +101,9 @@ typedef struct kvc_ring kvc_ring;   /* opaque host handle */
  * per-slot scales, scratch), or 0 if the config is invalid.
  *
  * Layout of dev_buf (for tests and tools; callers only need the size): one
- * slot for the m condition rows (none if m = 0) followed by W + 2 slots of n
- * rows (sink, W window chunks, one staging slot).  A slot of R rows stores,
+ * slot for the m condition rows (none if m = 0), one for the r reference rows
+ * (none if r = 0), W + 2 slots of n rows (sink, W window chunks, one staging
+ * slot) and one slot for the s source rows (none if s = 0).  A slot of R rows stores,
  * with P = R rounded up to KVC_TILE_KEYS and e = 2 (bf16) or 1 (fp8) bytes:
  *   K  [H][P][d]  (key-major)        -- rows >= R are zero
  *   Vt [H][d][P]  (value, transposed) -- columns permuted within tiles:
@@ -117,41 +134,50 @@ kvc_status kvc_create(const kvc_config* cfg, void* dev_buf, size_t bytes, kvc_ri
  * Write K/V rows into the cache (the fused cache-write kernel).
  *   kind = KVC_COND:   k, v are [m][H][d]; (re)writes the condition slot.
  *                      Allowed in any phase; m must be > 0.
- *   kind = KVC_STAGE:  k, v are [n][H][d], the current chunk's K/V for this
+ *   kind = KVC_REF:    k, v are [r][H][d]; (re)writes the reference slot.
+ *                      Allowed in any phase; r must be > 0.
+ *   kind = KVC_STAGE:  k, v are [n+s][H][d], the current chunk's K/V for this
  *                      denoise step.  From phase EMPTY it takes a free slot
  *                      as staging slot (KVC_E_STATE if none: the previous
  *                      chunk was not evicted); from STAGED it overwrites the
  *                      staging slot (next denoise step).  Not allowed when
  *                      COMMITTED (call kvc_evict first).
- *   kind = KVC_COMMIT: k, v are [n][H][d], the clean K/V of the current chunk
- *                      after its denoise steps.  Written into the staging slot
- *                      (or a free slot from phase EMPTY) and published: as the
- *                      sink if this is chunk 0, else as the newest window
- *                      chunk.  Not allowed when already COMMITTED.
+ *   kind = KVC_COMMIT: k, v are [n+s][H][d], the clean K/V of the current
+ *                      chunk after its denoise steps.  Written into the
+ *                      staging slot (or a free slot from phase EMPTY) and
+ *                      published: as the sink if this is chunk 0, else as the
+ *                      newest window chunk.  Not allowed when already
+ *                      COMMITTED.
+ *   For STAGE and COMMIT, rows 0..n-1 are the chunk's own tokens and rows
+ *   n..n+s-1 its source tokens (s = 0: none), which go to the source slot:
+ *   visible to this chunk's attention calls only, never published as history.
  * bf16 rings store bit copies; fp8 rings store E4M3 codes of x/s with
  * s = amax/448 per (head, slot), amax over that head's rows and features,
  * s = 1 when amax = 0 (nearest, ties to even, saturating).
  * The caller's k, v must stay valid until the stream reaches this work.
  * Errors: KVC_E_INVAL (null/misaligned pointers, unknown kind, COND with
- * m = 0), KVC_E_STATE, KVC_E_DEVICE.
+ * m = 0, REF with r = 0), KVC_E_STATE, KVC_E_DEVICE.
  */
 kvc_status kvc_append_chunk(kvc_ring* ring, int32_t kind, const void* k, const void* v,
                             void* stream);
 
 /*
  * Chunk-causal attention of the current chunk's queries.
- *   q    [n][H][d] bf16 queries of the current chunk.
- *   o    [n][H][d] bf16 output, o_i = sum_j softmax_j(scale <q_i, k_j>) v_j
- *        over the visible keys, in logical order [condition ; sink (chunk 0,
- *        for chunks >= 1) ; window chunks max(1, t-W) .. t-1 ; current chunk
- *        t].  Sink and window use committed clean K/V; the current chunk uses
- *        the staged K/V (phase STAGED) or its committed K/V (COMMITTED).
- *   lse  optional [H][n] float32 natural-log log-sum-exp of the scaled
+ *   q    [n+s][H][d] bf16 queries of the current chunk (its own n tokens,
+ *        then its s source tokens).
+ *   o    [n+s][H][d] bf16 output, o_i = sum_j softmax_j(scale <q_i, k_j>) v_j
+ *        over the visible keys, in logical order [condition ; reference ;
+ *        sink (chunk 0, for chunks >= 1) ; window chunks max(1, t-W) .. t-1 ;
+ *        current chunk t ; source tokens of chunk t].  Sink and window use
+ *        committed clean K/V; the current chunk and its source tokens use the
+ *        staged K/V (phase STAGED) or the committed K/V (COMMITTED).
+ *   lse  optional [H][n+s] float32 natural-log log-sum-exp of the scaled
  *        logits per query (NULL to skip).
  * q may not alias o.  No concatenated KV is formed: the kernel walks the
  * cache slots in logical order.
  * Errors: KVC_E_INVAL (null/misaligned pointers), KVC_E_STATE (phase EMPTY,
- * or condition tokens configured but never written), KVC_E_DEVICE.
+ * or condition or reference tokens configured but never written),
+ * KVC_E_DEVICE.
  */
 kvc_status chunk_attn_fwd(kvc_ring* ring, const void* q, void* o, float* lse, void* stream);
 
@@ -182,15 +208,16 @@ typedef struct kvc_info {
   int32_t kv_len;       /* keys an attention call would attend now, 0 if none */
   int32_t n_segments;   /* segments of that call */
   int32_t free_slots;   /* chunk slots holding nothing */
+  int32_t ref_valid;    /* reference slot written */
 } kvc_info;
 
 kvc_status kvc_get_info(const kvc_ring* ring, kvc_info* out);
 
 typedef struct kvc_segment {
-  int32_t chunk;        /* chunk id, or -1 for the condition tokens */
-  int32_t slot;         /* chunk slot index 0..W+1, or -1 for the condition slot */
+  int32_t chunk;        /* chunk id (source: the current chunk's), -1 for cond / ref */
+  int32_t slot;         /* chunk slot index 0..W+1, -1 cond, -3 ref, -4 source */
   int32_t rows;         /* valid rows */
-  int32_t role;         /* 0 cond, 1 sink, 2 window, 3 current */
+  int32_t role;         /* 0 cond, 1 sink, 2 window, 3 current, 4 ref, 5 source */
 } kvc_segment;
 
 /*
@@ -215,7 +242,9 @@ typedef struct kvc_slot_view {
 /*
  * Device addresses of one stored slot, for reading the cache back:
  * which = -1: condition slot; which = -2: the current chunk's slot (staged
- * or committed); which >= 0: the slot holding that committed chunk id.
+ * or committed); which = -3: reference slot; which = -4: source slot (while
+ * there is a current chunk); which >= 0: the slot holding that committed
+ * chunk id.
  * KVC_E_STATE if that slot holds nothing.
  */
 kvc_status kvc_get_slot(const kvc_ring* ring, int32_t which, kvc_slot_view* out);

@@ -35,6 +35,13 @@ ROLES = {
     "v_clean": 4,
     "k_cond": 5,
     "v_cond": 6,
+    "q_src": 7,
+    "k_src": 8,
+    "v_src": 9,
+    "k_src_clean": 10,
+    "v_src_clean": 11,
+    "k_ref": 12,
+    "v_ref": 13,
 }
 
 
@@ -52,6 +59,8 @@ class Workload:
     kv_dtype: str = "bf16"  # "bf16" or "fp8_e4m3"
     std: float = 1.0       # std of the N(0, std^2) draws (baseline distribution)
     seed: int = 0
+    ref_tokens: int = 0     # r: reference tokens (KV only, always visible)
+    source_tokens: int = 0  # s: source tokens per chunk (queried with the chunk)
 
     @property
     def scale(self) -> float:
@@ -73,6 +82,16 @@ WORKLOADS = {
     # fp8 e4m3 KV cache with per-(head, segment) fp32 scales, Q in bf16.
     "fp8": Workload("fp8", 40, 128, 1620, 256, 3, 32, kv_dtype="fp8_e4m3",
                     std=1.0 / math.sqrt(128), seed=4),
+    # all token groups of the editing model at the 720p chunk shape: the
+    # chunk's source-video tokens (one latent frame, 1620) are queried and
+    # attended with it, and a reference image (one latent frame) is visible to
+    # every chunk: 3240 queries over 11596 keys in steady state.
+    "groups": Workload("groups", 40, 128, 1620, 256, 3, 16, std=1.0 / math.sqrt(128),
+                       seed=5, ref_tokens=1620, source_tokens=1620),
+    # chunks of three latent frames (the chunk size of the LiveEdit pages):
+    # 4860 tokens per chunk, 256 + 5 * 4860 = 24556 keys in steady state.
+    "edit3": Workload("edit3", 40, 128, 4860, 256, 3, 12, std=1.0 / math.sqrt(128),
+                      seed=6),
 }
 
 # Alternative value distributions for parity runs (std of q, k, v).
@@ -151,6 +170,28 @@ class Stream:
         n = self.w.chunk_tokens
         return (self._t(layer, chunk, 0, "k_clean", n),
                 self._t(layer, chunk, 0, "v_clean", n))
+
+    def q_src(self, chunk: int, step: int = 0, layer: int = 0) -> torch.Tensor:
+        return self._t(layer, chunk, step, "q_src", self.w.source_tokens)
+
+    def kv_src(self, chunk: int, step: int = 0, layer: int = 0):
+        s = self.w.source_tokens
+        return (self._t(layer, chunk, step, "k_src", s),
+                self._t(layer, chunk, step, "v_src", s))
+
+    def kv_src_clean(self, chunk: int, layer: int = 0):
+        s = self.w.source_tokens
+        return (self._t(layer, chunk, 0, "k_src_clean", s),
+                self._t(layer, chunk, 0, "v_src_clean", s))
+
+    def kv_ref(self, layer: int = 0):
+        r = self.w.ref_tokens
+        if self.pool:
+            layer = layer % self.pool
+        return (draw(self.seed, layer, 0, 0, "k_ref", (r, self.w.heads, self.w.head_dim),
+                     _role_std(self.w, self.dist, "k_ref")),
+                draw(self.seed, layer, 0, 0, "v_ref", (r, self.w.heads, self.w.head_dim),
+                     _role_std(self.w, self.dist, "v_ref")))
 
     def kv_cond(self, layer: int = 0):
         m = self.w.cond_tokens

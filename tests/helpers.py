@@ -57,10 +57,14 @@ class StreamRun:
         self.heads = heads
         self.last_vmax = 0.0     # largest |v| of the current chunk's staged values
         ck, cv = stream.kv_cond() if self.w.cond_tokens else (None, None)
+        rk, rv = stream.kv_ref() if self.w.ref_tokens else (None, None)
         self.oracle = O1.StreamOracle(self.w.window, self.w.scale,
-                                      self._ref(ck), self._ref(cv))
+                                      self._ref(ck), self._ref(cv), self._ref(rk),
+                                      self._ref(rv))
         if ck is not None:
             ring.cond(ck.cuda(), cv.cuda())
+        if rk is not None:
+            ring.ref(rk.cuda(), rv.cuda())
 
     def _ref(self, x):
         if x is None:
@@ -77,19 +81,28 @@ class StreamRun:
         """Stage + attend every step, commit, evict.  Returns per-step
         (gpu_out, ref_out, stats)."""
         results = []
+        src = self.w.source_tokens > 0
         for step in range(self.w.steps):
             k, v = self.s.kv_noisy(t, step)
             q = self.s.q(t, step)
+            sk = sv = None
+            if src:
+                sk, sv = self.s.kv_src(t, step)
+                q = torch.cat([q, self.s.q_src(t, step)])
             self.last_vmax = float(np.abs(self._ref(v)).max())
-            self.ring.stage(k.cuda(), v.cuda())
-            lse_t = torch.empty(self.w.heads, self.w.chunk_tokens, dtype=torch.float32,
+            if src:
+                self.ring.stage(torch.cat([k, sk]).cuda(), torch.cat([v, sv]).cuda())
+            else:
+                self.ring.stage(k.cuda(), v.cuda())
+            lse_t = torch.empty(self.w.heads, q.shape[0], dtype=torch.float32,
                                 device="cuda") if lse else None
             o = self.ring.attention(q.cuda(), lse=lse_t)
             if check:
                 qr = O1.as_f64(q)
                 if self.heads is not None:
                     qr = qr[:, self.heads]
-                ref, ref_lse = self.oracle.attend(t, qr, self._ref(k), self._ref(v))
+                ref, ref_lse = self.oracle.attend(t, qr, self._ref(k), self._ref(v),
+                                                  src_k=self._ref(sk), src_v=self._ref(sv))
                 stats = compare(o, ref, self.heads)
                 if lse:
                     g = to_f64(lse_t)
@@ -100,7 +113,11 @@ class StreamRun:
             else:
                 results.append((o, None, None))
         kc, vc = self.s.kv_clean(t)
-        self.ring.commit(kc.cuda(), vc.cuda())
+        if src:
+            skc, svc = self.s.kv_src_clean(t)
+            self.ring.commit(torch.cat([kc, skc]).cuda(), torch.cat([vc, svc]).cuda())
+        else:
+            self.ring.commit(kc.cuda(), vc.cuda())
         self.oracle.commit(t, self._ref(kc), self._ref(vc))
         self.ring.evict()
         return results

@@ -30,7 +30,8 @@ def pi64(p):
 
 def fp8_ring(w):
     return kv.Ring(w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window,
-                   kv_dtype="fp8_e4m3")
+                   kv_dtype="fp8_e4m3", ref_tokens=w.ref_tokens,
+                   source_tokens=w.source_tokens)
 
 
 def fp8_workload(w, **kw):

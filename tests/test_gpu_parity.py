@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 
 def ring_for(w, **kw):
     return kv.Ring(w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window,
-                   kv_dtype=kw.get("kv_dtype", w.kv_dtype))
+                   kv_dtype=kw.get("kv_dtype", w.kv_dtype), ref_tokens=w.ref_tokens,
+                   source_tokens=w.source_tokens)
 
 
 # ---------------------------------------------------------------- K1 ----

@@ -23,8 +23,9 @@ class Record(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("rows", ctypes.c_int32), ("pitch", ctypes.c_int32),
                 ("nseg", ctypes.c_int32), ("dst_k", ctypes.c_uint64),
                 ("dst_vt", ctypes.c_uint64), ("src_k", ctypes.c_uint64),
-                ("src_v", ctypes.c_uint64), ("seg_k", ctypes.c_uint64 * 32),
-                ("seg_rows", ctypes.c_int32 * 32), ("seg_pitch", ctypes.c_int32 * 32),
+                ("src_v", ctypes.c_uint64), ("seg_k", ctypes.c_uint64 * kv.KVC_MAX_SEGMENTS),
+                ("seg_rows", ctypes.c_int32 * kv.KVC_MAX_SEGMENTS),
+                ("seg_pitch", ctypes.c_int32 * kv.KVC_MAX_SEGMENTS),
                 ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("k_scale", ctypes.c_uint64), ("stream", ctypes.c_uint64)]
 
@@ -44,9 +45,10 @@ def lib():
 
 
 class FakeRing:
-    def __init__(self, L, H=2, d=128, n=100, m=40, W=2, dtype=kv.KVC_KV_BF16, scale=0.0):
+    def __init__(self, L, H=2, d=128, n=100, m=40, W=2, dtype=kv.KVC_KV_BF16, scale=0.0,
+                 r=0, s=0):
         self.L = L
-        self.cfg = kv.kvc_config(H, d, n, m, W, dtype, scale)
+        self.cfg = kv.kvc_config(H, d, n, m, W, dtype, scale, r, s)
         self.bytes = L.kvc_required_bytes(ctypes.byref(self.cfg))
         assert self.bytes > 0
         self.h = ctypes.c_void_p()
@@ -98,7 +100,7 @@ class FakeRing:
         self.L.kvc_destroy(self.h)
 
 
-def expected_bytes(H, d, n, m, W, e, fp8):
+def expected_bytes(H, d, n, m, W, e, fp8, r=0, s=0):
     al = lambda x: (x + 255) // 256 * 256
     P = lambda r: (r + 63) // 64 * 64
     def slot(r):
@@ -106,12 +108,14 @@ def expected_bytes(H, d, n, m, W, e, fp8):
         if fp8:
             b += al(8 * H)
         return b
-    total = (slot(m) if m else 0) + (W + 2) * slot(n)
+    total = (slot(m) if m else 0) + (slot(r) if r else 0) + (W + 2) * slot(n) + \
+        (slot(s) if s else 0)
     if fp8:
-        total += al(4 * 2 * H * (P(max(n, m)) // 64))
-    # attention workspace: 2 counters per 128-query row, then 2 partial slots
-    # per persistent workgroup (512 at most): max + 2 sums and fp32 O [128][d]
-    rows = H * ((n + 127) // 128)
+        total += al(4 * 2 * H * (P(max(n, m, r, s)) // 64))
+    # attention workspace: 2 counters per 128-query row (n + s queries), then 2
+    # partial slots per persistent workgroup (512 at most): max + 2 sums and
+    # fp32 O [128][d]
+    rows = H * ((n + s + 127) // 128)
     total += al(8 * rows) + al(4 * 2 * 512 * 3 * 128) + 4 * 2 * 512 * 128 * d
     return total
 
@@ -119,10 +123,11 @@ def expected_bytes(H, d, n, m, W, e, fp8):
 @pytest.mark.parametrize("H,d,n,m,W", [(40, 128, 1620, 256, 3), (1, 64, 64, 16, 2),
                                        (3, 128, 7, 0, 0), (2, 64, 65, 1, 29)])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_required_bytes_matches_layout(lib, H, d, n, m, W, fp8):
-    cfg = kv.kvc_config(H, d, n, m, W, int(fp8), 0.0)
+@pytest.mark.parametrize("r,s", [(0, 0), (30, 0), (0, 70), (1620, 1620)])
+def test_required_bytes_matches_layout(lib, H, d, n, m, W, fp8, r, s):
+    cfg = kv.kvc_config(H, d, n, m, W, int(fp8), 0.0, r, s)
     assert lib.kvc_required_bytes(ctypes.byref(cfg)) == \
-        expected_bytes(H, d, n, m, W, 1 if fp8 else 2, fp8)
+        expected_bytes(H, d, n, m, W, 1 if fp8 else 2, fp8, r, s)
 
 
 def test_720p_ring_size():
@@ -136,6 +141,7 @@ def test_720p_ring_size():
     dict(heads=0), dict(head_dim=96), dict(chunk_tokens=0), dict(cond_tokens=-1),
     dict(window=-1), dict(window=30), dict(kv_dtype=2), dict(softmax_scale=-1.0),
     dict(softmax_scale=float("nan")), dict(softmax_scale=float("inf")),
+    dict(ref_tokens=-1), dict(source_tokens=-5), dict(source_tokens=(1 << 20) + 1),
 ])
 def test_bad_configs_rejected(lib, bad):
     f = dict(heads=2, head_dim=128, chunk_tokens=10, cond_tokens=4, window=2, kv_dtype=0,
@@ -377,3 +383,62 @@ def test_product_e4m3_encoder_matches_oracle(lib):
     out = np.empty(x.size, np.uint8)
     lib.kvcfake_e4m3_encode(x.ctypes.data, out.ctypes.data, x.size)
     np.testing.assert_array_equal(out, O3.encode(x))
+
+
+@pytest.mark.parametrize("W", [0, 2, 3])
+@pytest.mark.parametrize("m,rr,s", [(40, 30, 70), (0, 30, 0), (0, 0, 70), (40, 0, 70)])
+def test_token_groups(lib, W, m, rr, s):
+    # reference tokens: one always-visible segment after cond; source tokens:
+    # written from rows n.. of each STAGE/COMMIT into their own slot, attended
+    # by (and queried with) the current chunk only, never published as history
+    H, d, n = 2, 128, 100
+    r = FakeRing(lib, H=H, d=d, n=n, m=m, W=W, r=rr, s=s)
+    row_bytes = H * d * 2
+    if m:
+        assert r.append(kv.KVC_COND) == kv.KVC_OK
+    if not rr:
+        assert r.append(kv.KVC_REF) == kv.KVC_E_INVAL
+    st, _ = r.slot(-3)
+    assert st == kv.KVC_E_STATE
+    for t in range(W + 4):
+        before = r.count()
+        assert r.append(kv.KVC_STAGE, k=0x10000, v=0x20000) == kv.KVC_OK
+        writes = r.count() - before
+        assert writes == (2 if s else 1)
+        if s:
+            w = r.last()
+            assert (w.kind, w.rows, w.src_k, w.src_v) == \
+                (0, s, 0x10000 + n * row_bytes, 0x20000 + n * row_bytes)
+            st, view = r.slot(-4)
+            assert st == kv.KVC_OK and view.rows == s and w.dst_k == view.k
+        if rr and t == 0:
+            assert r.attn() == kv.KVC_E_STATE        # reference configured, not written
+            assert r.append(kv.KVC_REF) == kv.KVC_OK
+            st, view = r.slot(-3)
+            assert st == kv.KVC_OK and view.rows == rr
+            assert r.last().rows == rr and r.last().dst_k == view.k
+        assert r.attn() == kv.KVC_OK
+        a = r.last()
+        assert a.kind == 1 and a.rows == n + s
+        segs = r.segments()
+        roles = [x[3] for x in segs]
+        want = ([0] if m else []) + ([4] if rr else []) + ([1] if t >= 1 else []) + \
+            [2] * min(W, max(t - 1, 0)) + [3] + ([5] if s else [])
+        assert roles == want
+        assert [x[2] for x in segs] == [{0: m, 4: rr, 5: s}.get(x, n) for x in roles]
+        assert a.nseg == len(segs)
+        assert list(a.seg_rows[:a.nseg]) == [x[2] for x in segs]
+        assert r.info()["kv_len"] == O1.kv_length(t, m, n, W, rr, s)
+        before = r.count()
+        assert r.append(kv.KVC_COMMIT, k=0x30000, v=0x40000) == kv.KVC_OK
+        assert r.count() - before == (2 if s else 1)
+        assert r.evict()[0] == kv.KVC_OK
+        if s:
+            st, _ = r.slot(-4)
+            assert st == kv.KVC_E_STATE                # no current chunk
+    # the history holds chunk tokens only: every committed slot has n rows
+    for cid in range(W + 4):
+        st, view = r.slot(cid)
+        if st == kv.KVC_OK:
+            assert view.rows == n
+    r.close()
