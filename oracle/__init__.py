@@ -24,12 +24,15 @@ pages describe in words):
   loop: denoise with the cache as history, then update the cache keeping only
   the window and the head sink).
 * aitrends.kr, LiveEdit summary, glossary entry on chunk-wise causal attention:
-  a chunk sees itself and earlier chunks only.
+  a chunk sees itself and earlier chunks only; methodology and technical
+  detail sections: the AR-oriented Mask Cache (active rows by the L2
+  distance of the previous chunk's edited and source latents).
 
 Modules:
   attention  -- O1: explicit KV assembly + fp64 naive softmax attention.
   brute      -- O2: whole-stream attention under a block-causal window mask.
   fp8        -- O3: OCP e4m3 codec and the per-(head, segment) scale rule.
+  liveedit   -- O4: LiveEdit's active-row mask and active-row attention.
 
 Readings where the pages are silent (each is listed in the design notes):
   * W counts past chunks only; the sink and the current chunk come on top.
@@ -45,4 +48,4 @@ tests/test_fp8_codec.py (brute force, closed forms, library routines,
 invariants).  None is "parity unpinned".
 """
 
-from . import attention, brute, fp8  # noqa: F401
+from . import attention, brute, fp8, liveedit  # noqa: F401
