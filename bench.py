@@ -30,9 +30,24 @@ PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0
 
 
-def attn_flops(w, kv_len: int) -> float:
-    """QK^T + PV of one call: the chunk's own and source queries over kv_len keys."""
-    return 4.0 * (w.chunk_tokens + w.source_tokens) * kv_len * w.head_dim * w.heads
+def attn_flops(w, kv_len: int, queries: int | None = None) -> float:
+    """QK^T + PV of one call: the chunk's own and source queries (or the
+    active rows of an active-row call) over kv_len keys."""
+    if queries is None:
+        queries = w.chunk_tokens + w.source_tokens
+    return 4.0 * queries * kv_len * w.head_dim * w.heads
+
+
+def active_keep(w, frac: float) -> int:
+    return int(round(frac * (w.chunk_tokens + w.source_tokens)))
+
+
+def latent_grid(nq: int):
+    """(grid, frames) of the synthetic LiveEdit latents of an nq-token chunk:
+    30x54 frames (the 720p latent grid) when nq is a multiple of 1620."""
+    if nq % 1620 == 0:
+        return (30, 54), nq // 1620
+    return (1, nq), 1
 
 
 def cpu_baseline(w, seconds: float, seed_dist: str = "baseline") -> dict:
@@ -100,7 +115,7 @@ def _cpu_model() -> str:
 class Inputs:
     """Per-chunk inputs uploaded once (a pool of `pool` chunk sets)."""
 
-    def __init__(self, w, pool: int, dist: str, device):
+    def __init__(self, w, pool: int, dist: str, device, active_rows: bool = False):
         import torch
         import synth
         s = synth.Stream(w, dist)
@@ -127,6 +142,13 @@ class Inputs:
             self.noisy.append(noisy)
             self.clean.append((up(k, sk), up(v, sv)))
         self.pool = pool
+        # LiveEdit: the previous chunk's (source, edited) latents, 16 channels
+        self.latents = []
+        if active_rows:
+            grid, frames = latent_grid(w.chunk_tokens + w.source_tokens)
+            self.latents = [tuple(x.to(device) for x in
+                                  synth.edit_latents(w.seed, c, grid, frames, 16))
+                            for c in range(pool)]
 
 
 def run_stream_bench(w, args, device, flat: bool):
@@ -140,7 +162,11 @@ def run_stream_bench(w, args, device, flat: bool):
     import chunked_attention_amd as kv
 
     pool = min(args.pool, w.chunks) if args.pool else w.chunks
-    inp = Inputs(w, pool, args.dist, device)
+    inp = Inputs(w, pool, args.dist, device, active_rows=args.active_rows is not None)
+    keep = active_keep(w, args.active_rows) if args.active_rows is not None else None
+    nq = w.chunk_tokens + w.source_tokens
+    rows_buf = torch.empty(nq, dtype=torch.int32, device=device)
+    count_buf = torch.empty(1, dtype=torch.int32, device=device)
     def new_rings():
         rs = [kv.Ring(w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window,
                       kv_dtype=w.kv_dtype, device=device, ref_tokens=w.ref_tokens,
@@ -163,10 +189,10 @@ def run_stream_bench(w, args, device, flat: bool):
         warmup, steps = args.warmup, w.chunks
     else:
         warmup, steps = args.warmup, args.steps
-    per_step = w.steps * w.layers * 3 + w.layers * 4 + 1
+    per_step = w.steps * w.layers * 4 + w.layers * 4 + 1
     pool_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * per_step + 2)]
     ev_iter = iter(pool_ev)
-    attn_events, write_events, step_events = [], [], []
+    attn_events, write_events, step_events, mask_events = [], [], [], []
     kv_len = [0]        # keys attended by the timed calls (largest)
 
     def chunk(t: int, timed: bool):
@@ -175,6 +201,23 @@ def run_stream_bench(w, args, device, flat: bool):
             e = next(ev_iter)
             e.record(stream)
             step_events.append(e)
+        if keep is not None:
+            # LiveEdit: this chunk's active rows from the previous chunk's
+            # latents, on the device (shared by every layer and step)
+            if timed:
+                m0, m1 = next(ev_iter), next(ev_iter)
+                m0.record(stream)
+            kv.kvc_edit_mask(*inp.latents[c], keep=keep, rows=rows_buf, count=count_buf)
+            if timed:
+                m1.record(stream)
+                mask_events.append((m0, m1))
+
+        def attend(r, q, out):
+            if keep is None:
+                r.attention(q, out=out)
+            else:
+                r.attention_rows(q, rows_buf, count_buf, out=out)
+
         for st in range(w.steps):
             for li, r in enumerate(rings):
                 if timed:
@@ -182,7 +225,7 @@ def run_stream_bench(w, args, device, flat: bool):
                     e0.record(stream)
                     r.stage(*inp.noisy[c][st])
                     e1.record(stream)
-                    r.attention(inp.q[c][st], out=outs[li & 1])
+                    attend(r, inp.q[c][st], outs[li & 1])
                     e2.record(stream)
                     if li == 0:
                         kv_len[0] = max(kv_len[0], r.info().kv_len)
@@ -190,7 +233,7 @@ def run_stream_bench(w, args, device, flat: bool):
                     attn_events.append((e1, e2))
                 else:
                     r.stage(*inp.noisy[c][st])
-                    r.attention(inp.q[c][st], out=outs[li & 1])
+                    attend(r, inp.q[c][st], outs[li & 1])
         for li, r in enumerate(rings):
             if timed:
                 e0, e1 = next(ev_iter), next(ev_iter)
@@ -203,13 +246,13 @@ def run_stream_bench(w, args, device, flat: bool):
                     # the committed chunk (queries of the clean latent; the
                     # first step's stand in)
                     e2 = next(ev_iter)
-                    r.attention(inp.q[c][0], out=outs[li & 1])
+                    attend(r, inp.q[c][0], outs[li & 1])
                     e2.record(stream)
                     attn_events.append((e1, e2))
             else:
                 r.commit(*inp.clean[c])
                 if args.clean_pass:
-                    r.attention(inp.q[c][0], out=outs[li & 1])
+                    attend(r, inp.q[c][0], outs[li & 1])
             r.evict()
 
     def clock_warmup(t: int) -> int:
@@ -274,6 +317,7 @@ def run_stream_bench(w, args, device, flat: bool):
         "warmup": warmup,
         "attn_ms": [a.elapsed_time(b) for a, b in attn_events],
         "write_ms": [a.elapsed_time(b) for a, b in write_events],
+        "mask_ms": [a.elapsed_time(b) for a, b in mask_events],
         "step_ms": step_ms,
         "kv_len": kv_len[0],
         "first_chunk": t_first,
@@ -378,6 +422,9 @@ def main() -> int:
                     help="override the config's window W (e.g. the long stream at W=3)")
     ap.add_argument("--clean-pass", action="store_true",
                     help="one more attention call per layer after each COMMIT (clean pass)")
+    ap.add_argument("--active-rows", type=float, default=None, metavar="FRAC",
+                    help="LiveEdit: each chunk attends only the top FRAC of its rows by the "
+                         "edit distance of the previous chunk's latents (mask on the device)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -409,7 +456,8 @@ def main() -> int:
         return 2
 
     r = run_stream_bench(w, args, device, flat)
-    flops = attn_flops(w, r["kv_len"])
+    queries = active_keep(w, args.active_rows) if args.active_rows is not None else None
+    flops = attn_flops(w, r["kv_len"], queries)
     if flat:
         # throughput over the window-full chunks only
         steady = slice(w.window + 1, None)
@@ -448,7 +496,8 @@ def main() -> int:
             "workload": f"{w.name}: H={w.heads} d={w.head_dim} n={w.chunk_tokens} "
                         f"m={w.cond_tokens} r={w.ref_tokens} s={w.source_tokens} "
                         f"W={w.window} layers={w.layers} steps={w.steps}"
-                        f"{' +clean pass' if args.clean_pass else ''}, "
+                        f"{' +clean pass' if args.clean_pass else ''}"
+                        f"{f' active rows {queries} (top-k edit mask)' if queries is not None else ''}, "
                         f"steady-state chunks {r['first_chunk']}..{r['last_chunk']} "
                         f"(|S|={r['kv_len']} keys); one step = STAGE + attention per "
                         f"denoise step and layer, COMMIT + evict per layer",
@@ -457,6 +506,7 @@ def main() -> int:
             "layers": w.layers, "denoise_steps": w.steps, "kv_dtype": w.kv_dtype,
             "ref_tokens": w.ref_tokens, "source_tokens": w.source_tokens,
             "clean_pass": args.clean_pass,
+            "active_rows": queries,
         },
         "chunks_per_s": round(1.0 / step_s, 2),
         "pct_mfma_peak": round(100 * value / peak, 2),
@@ -466,6 +516,8 @@ def main() -> int:
         "attn_gflop_per_call": round(flops / 1e9, 3),
         "cache_write_median_us": round(write_us, 2),
         "cache_write_gbps": round(write_bytes / (write_us * 1e-6) / 1e9, 1),
+        "edit_mask_median_us": (round(statistics.median(r["mask_ms"]) * 1e3, 2)
+                                if r["mask_ms"] else None),
         "step_ms_median": round(med, 4),
         "step_ms_max_dev_pct": dev(steps_ms, med),
         "roofline": {

@@ -39,6 +39,8 @@ KVC_MAX_WINDOW = 29
 KVC_MAX_SEGMENTS = KVC_MAX_WINDOW + 5
 KVC_TILE_KEYS = 64
 KVC_ALIGN = 256
+KVC_MAX_MASK_TOKENS = 16384
+KVC_MAX_MASK_CHANNELS = 4096
 
 _DTYPES = {"bf16": KVC_KV_BF16, "fp8_e4m3": KVC_KV_FP8_E4M3}
 
@@ -71,6 +73,7 @@ class kvc_slot_view(ctypes.Structure):
 EXPORTS = (
     "kvc_required_bytes", "kvc_create", "kvc_append_chunk", "chunk_attn_fwd", "kvc_evict",
     "kvc_destroy", "kvc_status_str", "kvc_get_info", "kvc_get_segments", "kvc_get_slot",
+    "chunk_attn_fwd_rows", "kvc_edit_mask",
 )
 
 
@@ -87,6 +90,10 @@ def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.kvc_append_chunk.restype = I
     lib.chunk_attn_fwd.argtypes = [P, P, P, P, P]
     lib.chunk_attn_fwd.restype = I
+    lib.chunk_attn_fwd_rows.argtypes = [P, P, P, P, P, P, P]
+    lib.chunk_attn_fwd_rows.restype = I
+    lib.kvc_edit_mask.argtypes = [P, P, I, I, ctypes.c_float, I, P, P, P]
+    lib.kvc_edit_mask.restype = I
     lib.kvc_evict.argtypes = [P, ctypes.POINTER(I)]
     lib.kvc_evict.restype = I
     lib.kvc_destroy.argtypes = [P]
@@ -184,7 +191,7 @@ def kvc_append_chunk(handle, cfg: kvc_config, kind: int, k, v, stream=None) -> N
            "kvc_append_chunk")
 
 
-def chunk_attn_fwd(handle, cfg: kvc_config, q, o, lse=None, stream=None) -> None:
+def _attn_args(cfg: kvc_config, q, o, lse):
     import torch
     nq = query_rows(cfg)
     _check_tokens(q, nq, cfg, "q")
@@ -196,9 +203,61 @@ def chunk_attn_fwd(handle, cfg: kvc_config, q, o, lse=None, stream=None) -> None
             raise ValueError("lse must be a contiguous float32 [heads, chunk_tokens + "
                              "source_tokens] tensor")
         lse_ptr = lse.data_ptr()
-    _check(lib().chunk_attn_fwd(handle, ctypes.c_void_p(q.data_ptr()),
-                                ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(lse_ptr),
-                                _stream_handle(stream)), "chunk_attn_fwd")
+    return ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(lse_ptr)
+
+
+def _check_i32(x, what: str, numel: int | None = None) -> None:
+    import torch
+    if x.dtype != torch.int32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous int32 CUDA tensor")
+    if numel is not None and x.numel() < numel:
+        raise ValueError(f"{what} needs at least {numel} elements")
+
+
+def chunk_attn_fwd(handle, cfg: kvc_config, q, o, lse=None, stream=None) -> None:
+    _check(lib().chunk_attn_fwd(handle, *_attn_args(cfg, q, o, lse), _stream_handle(stream)),
+           "chunk_attn_fwd")
+
+
+def chunk_attn_fwd_rows(handle, cfg: kvc_config, q, o, rows, count, lse=None,
+                        stream=None) -> None:
+    """Attention of rows[:count] of q only; the other rows of o (and lse) are
+    left as they are.  rows/count are device int32 tensors (count: 1 element)."""
+    _check_i32(rows, "rows", query_rows(cfg))
+    _check_i32(count, "count", 1)
+    _check(lib().chunk_attn_fwd_rows(handle, *_attn_args(cfg, q, o, lse),
+                                     ctypes.c_void_p(rows.data_ptr()),
+                                     ctypes.c_void_p(count.data_ptr()),
+                                     _stream_handle(stream)), "chunk_attn_fwd_rows")
+
+
+def kvc_edit_mask(z_src, z_edit, tau: float | None = None, keep: int | None = None, rows=None,
+                  count=None, stream=None):
+    """LiveEdit's active rows: (rows [tokens] int32, count [1] int32), device
+    tensors.  Give tau (threshold mode) or keep (top-k mode)."""
+    import torch
+    if (tau is None) == (keep is None):
+        raise ValueError("give exactly one of tau and keep")
+    for z, what in ((z_src, "z_src"), (z_edit, "z_edit")):
+        if z.dtype != torch.bfloat16 or not z.is_cuda or not z.is_contiguous() or z.dim() != 2:
+            raise ValueError(f"{what} must be a contiguous 2-d bf16 CUDA tensor")
+    if z_src.shape != z_edit.shape:
+        raise ValueError("z_src and z_edit differ in shape")
+    tokens, channels = z_src.shape
+    if rows is None:
+        rows = torch.empty(tokens, dtype=torch.int32, device=z_src.device)
+    if count is None:
+        count = torch.empty(1, dtype=torch.int32, device=z_src.device)
+    _check_i32(rows, "rows", tokens)
+    _check_i32(count, "count", 1)
+    _check(lib().kvc_edit_mask(ctypes.c_void_p(z_src.data_ptr()),
+                               ctypes.c_void_p(z_edit.data_ptr()), tokens, channels,
+                               0.0 if tau is None else float(tau),
+                               -1 if keep is None else int(keep),
+                               ctypes.c_void_p(rows.data_ptr()),
+                               ctypes.c_void_p(count.data_ptr()), _stream_handle(stream)),
+           "kvc_edit_mask")
+    return rows, count
 
 
 def kvc_evict(handle) -> int:
@@ -274,6 +333,11 @@ class Ring:
         if out is None:
             out = torch.empty_like(q)
         chunk_attn_fwd(self.handle, self.cfg, q, out, lse, stream)
+        return out
+
+    def attention_rows(self, q, rows, count, out, lse=None, stream=None):
+        """Active-row attention: only rows[:count] of `out` are written."""
+        chunk_attn_fwd_rows(self.handle, self.cfg, q, out, rows, count, lse, stream)
         return out
 
     def evict(self) -> int:

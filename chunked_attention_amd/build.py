@@ -25,7 +25,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 HOST_LIB = os.path.join(BUILD, "libkvc_hostcheck.so")
 
-HIP_SOURCES = ["cache_write.hip", "attn_fwd.hip", "attn_fwd_fp8.hip"]
+HIP_SOURCES = ["cache_write.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "edit_mask.hip"]
 CPP_SOURCES = ["ring.cpp", "plan.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -48,18 +48,22 @@ struct AttnArgs {
   const uint16_t* q;
   uint16_t* o;
   float* lse;
+  const int* qrows;         // active-row calls: query i is row qrows[i] of q / o / lse
+  const int* qcount;        // active-row calls: number of active rows (device memory)
   float* part_o;            // [2*nwg][kBq*D] partial O, accumulator layout
   float* part_ml;           // [2*nwg][waves][3][32] partial reference, sum, exact sum
   unsigned* counters;       // [nrows][2]: arrived, partials written
-  int n;
+  int n;                    // queries of the call (active-row calls: at most)
+  int ld;                   // rows of q / o; row stride of lse
   int heads;
   float c;                  // softmax scale * log2(e)
   int nseg;
   int ntiles;               // steps per row (T; a step is a kernel-defined key count)
+  int step_keys;            // keys per step
   int nqt;                  // rows per head
-  int nrows;                // heads * nqt
+  int nrows;                // heads * nqt (active-row calls: at most)
   int nwg;                  // persistent workgroups
-  long long total;          // nrows * ntiles
+  long long total;          // nrows * ntiles (active-row calls: at most)
   SegArg seg[kMaxSegments];
 };
 
@@ -76,12 +80,40 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// first step of workgroup w's range, and the owner of step x
-__device__ __forceinline__ long long range_begin(long long w, const AttnArgs& a) {
-  return w * a.total / a.nwg;
+// The call's work: queries, 128-query rows per head and (row, step) pairs.
+// An active-row call reads its query count from device memory (written by an
+// earlier kernel on the stream), so the split is taken at run time: the grid
+// is sized for every row, and workgroups whose range is empty exit.
+struct Split {
+  long long total;          // heads * nqt * ntiles
+  int nqt;
+  int nq;
+  int nwg;                  // workgroups with work (the rest exit)
+};
+__device__ __forceinline__ Split make_split(const AttnArgs& a) {
+  if (!a.qcount) return Split{a.total, a.nqt, a.n, a.nwg};
+  const int nq = min(max(*a.qcount, 0), a.n);
+  const int nqt = (nq + kBq - 1) / kBq;
+  const long long total = static_cast<long long>(a.heads) * nqt * a.ntiles;
+  // as on the host: pieces of at least kMinPieceKeys keys
+  const long long by_size = max(1LL, total * a.step_keys / kMinPieceKeys);
+  return Split{total, nqt, nq, static_cast<int>(min(static_cast<long long>(a.nwg), by_size))};
 }
-__device__ __forceinline__ int owner_of(long long x, const AttnArgs& a) {
-  return static_cast<int>(((x + 1) * a.nwg - 1) / a.total);
+// row of q / o / lse that query qi of the call stands for, or -1 if none
+// (past the active count, or an index outside the tensors)
+__device__ __forceinline__ int query_row(const AttnArgs& a, const Split& sp, int qi) {
+  if (qi >= sp.nq) return -1;
+  if (!a.qrows) return qi;
+  const int g = a.qrows[qi];
+  return g >= 0 && g < a.ld ? g : -1;
+}
+
+// first step of workgroup w's range, and the owner of step x
+__device__ __forceinline__ long long range_begin(long long w, const Split& sp) {
+  return w * sp.total / sp.nwg;
+}
+__device__ __forceinline__ int owner_of(long long x, const Split& sp) {
+  return static_cast<int>(((x + 1) * sp.nwg - 1) / sp.total);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -226,14 +258,15 @@ template <int D, bool kLse>
 __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)[D / 32],
                                              float m_run, float l_tot, float le_tot, int r,
                                              int h, int qbase, bool first_piece, int w,
-                                             int wave, int lane, unsigned& s_ticket) {
+                                             int wave, int lane, unsigned& s_ticket,
+                                             const Split& sp) {
   constexpr int kDB = D / 32;
   const int tid = threadIdx.x;
   const int col = lane & 31;
   const int half = lane >> 5;
   const long long rs = static_cast<long long>(r) * a.ntiles;
-  const int w_lo = owner_of(rs, a);
-  const int w_hi = owner_of(rs + a.ntiles - 1, a);
+  const int w_lo = owner_of(rs, sp);
+  const int w_hi = owner_of(rs + a.ntiles - 1, sp);
   if (w_hi > w_lo) {
     // this row is split: the last piece to arrive merges the others
     unsigned* arrived = a.counters + 2 * r;
@@ -287,7 +320,7 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
     float mmax = m_run;
     for (int ow = w_lo; ow <= w_hi; ++ow) {
       if (ow == w) continue;
-      const int oslot = range_begin(ow, a) >= rs ? 0 : 1;
+      const int oslot = range_begin(ow, sp) >= rs ? 0 : 1;
       const float* pml = a.part_ml + static_cast<size_t>(2 * ow + oslot) * kWaves * kMl + ml_wave;
       mmax = fmaxf(mmax, __hip_atomic_load(pml + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     }
@@ -301,7 +334,7 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
 #pragma unroll
         for (int db = 0; db < kDB; ++db) v[db] = oacc[db];
       } else {
-        const int oslot = range_begin(ow, a) >= rs ? 0 : 1;
+        const int oslot = range_begin(ow, sp) >= rs ? 0 : 1;
         const float* po = a.part_o + static_cast<size_t>(2 * ow + oslot) * kBq * D + o_wave;
         const float* pml =
             a.part_ml + static_cast<size_t>(2 * ow + oslot) * kWaves * kMl + ml_wave;
@@ -334,10 +367,10 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
     }
   }
 
-  const int qi = qbase + col;
-  if (qi >= a.n) return;
+  const int g = query_row(a, sp, qbase + col);
+  if (g < 0) return;
   const float inv = 1.0f / l_tot;
-  uint16_t* orow = a.o + (static_cast<size_t>(qi) * a.heads + h) * D;
+  uint16_t* orow = a.o + (static_cast<size_t>(g) * a.heads + h) * D;
 #pragma unroll
   for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -353,7 +386,7 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
       *reinterpret_cast<uint2*>(orow + db * 32 + g * 8 + half * 4) = make_uint2(wv[0], wv[1]);
     }
   if (kLse && half == 0)
-    a.lse[static_cast<size_t>(h) * a.n + qi] = (m_run + __log2f(le_tot)) * kLn2;
+    a.lse[static_cast<size_t>(h) * a.ld + g] = (m_run + __log2f(le_tot)) * kLn2;
 }
 
 // Host side: kernel arguments from a launch description (segment table in

@@ -184,25 +184,28 @@ void attn_fwd_bf16(const AttnArgs a) {
     return xor32_max(mx) * a.c;
   };
 
-  for (long long x = range_begin(w, a), xe = range_begin(w + 1, a); x < xe;) {
+  const Split sp = make_split(a);
+  if (w >= sp.nwg) return;
+  for (long long x = range_begin(w, sp), xe = range_begin(w + 1, sp); x < xe;) {
     const int r = static_cast<int>(x / a.ntiles);
     const int t0 = static_cast<int>(x % a.ntiles);
     const long long rest = xe - x;
     const int t1 = rest < a.ntiles - t0 ? t0 + static_cast<int>(rest) : a.ntiles;
-    const bool first_piece = x == range_begin(w, a);
+    const bool first_piece = x == range_begin(w, sp);
     x += t1 - t0;
-    const int h = r / a.nqt;
-    const int qbase = (r - h * a.nqt) * kBq + wave * kQW;
+    const int h = r / sp.nqt;
+    const int qbase = (r - h * sp.nqt) * kBq + wave * kQW;
 
     // Q^T as B operand: lane holds query qbase + col, features
     // ks*16 + half*8 .. +7
     bf16x8_t qreg[kDS];
     {
-      const int qi = qbase + col;
-      const uint16_t* qrow = a.q + (static_cast<size_t>(qi) * a.heads + h) * D + half * 8;
+      const int g = query_row(a, sp, qbase + col);
+      const uint16_t* qrow = a.q + (static_cast<size_t>(g < 0 ? 0 : g) * a.heads + h) * D +
+                             half * 8;
 #pragma unroll
       for (int ks = 0; ks < kDS; ++ks) {
-        if (qi < a.n) {
+        if (g >= 0) {
           qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
         } else {
 #pragma unroll
@@ -376,7 +379,7 @@ void attn_fwd_bf16(const AttnArgs a) {
     }
 
     finish_piece<D, kLse>(a, oacc, m_ref, l_tot, le_tot, r, h, qbase, first_piece, w, wave,
-                          lane, s_ticket);
+                          lane, s_ticket, sp);
   }
 }
 
@@ -422,7 +425,10 @@ kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a) {
   a.q = static_cast<const uint16_t*>(d.q);
   a.o = static_cast<uint16_t*>(d.o);
   a.lse = d.lse;
+  a.qrows = d.qrows;
+  a.qcount = d.qcount;
   a.n = d.n;
+  a.ld = d.n;
   a.heads = d.heads;
   a.c = d.scale * kLog2e;
   a.nseg = d.nseg;
@@ -441,6 +447,7 @@ kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a) {
     tiles += (d.seg[s].rows + step_keys - 1) / step_keys;
   }
   a.ntiles = tiles;
+  a.step_keys = step_keys;
   a.nqt = (d.n + kBq - 1) / kBq;
   a.nrows = a.nqt * d.heads;
   a.total = static_cast<long long>(a.nrows) * a.ntiles;

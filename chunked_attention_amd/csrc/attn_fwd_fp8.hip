@@ -200,15 +200,17 @@ void attn_fwd_fp8(const AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = 0x38383838;   // E4M3 1.0 in every byte
 
-  for (long long x = range_begin(w, a), xe = range_begin(w + 1, a); x < xe;) {
+  const Split sp = make_split(a);
+  if (w >= sp.nwg) return;
+  for (long long x = range_begin(w, sp), xe = range_begin(w + 1, sp); x < xe;) {
     const int r = static_cast<int>(x / a.ntiles);
     const int t0 = static_cast<int>(x % a.ntiles);
     const long long rest = xe - x;
     const int t1 = rest < a.ntiles - t0 ? t0 + static_cast<int>(rest) : a.ntiles;
-    const bool first_piece = x == range_begin(w, a);
+    const bool first_piece = x == range_begin(w, sp);
     x += t1 - t0;
-    const int h = r / a.nqt;
-    const int qbase = (r - h * a.nqt) * kBq + wave * kQW;
+    const int h = r / sp.nqt;
+    const int qbase = (r - h * sp.nqt) * kBq + wave * kQW;
 
     // Q^T as B operands: lane holds query qbase + col, byte j of k-step ks
     // = feature ks*64 + half*32 + j.  q / s_q = Q8hi + Q8lo / 16 (E4M3 of
@@ -217,15 +219,16 @@ void attn_fwd_fp8(const AttnArgs a) {
     i32x8_t q8[kKS], q8lo[kKS];
     float cq;   // scale * log2(e) * s_q
     {
-      const int qi = qbase + col;
+      const int g = query_row(a, sp, qbase + col);
       float qv[kKS][32];
-      const uint16_t* qrow = a.q + (static_cast<size_t>(qi) * a.heads + h) * D + half * 32;
+      const uint16_t* qrow = a.q + (static_cast<size_t>(g < 0 ? 0 : g) * a.heads + h) * D +
+                             half * 32;
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           uint4 u = make_uint4(0, 0, 0, 0);
-          if (qi < a.n) u = ld16(qrow + ks * 64 + c4 * 8);
+          if (g >= 0) u = ld16(qrow + ks * 64 + c4 * 8);
           const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -418,7 +421,7 @@ void attn_fwd_fp8(const AttnArgs a) {
       for (int i = 0; i < 16; ++i) oacc[db][i] *= vs_cur;
     const float l_tot = lacc[0];
     finish_piece<D, kLse>(a, oacc, m_ref, l_tot, l_tot, r, h, qbase, first_piece, w, wave, lane,
-                          s_ticket);
+                          s_ticket, sp);
   }
 }
 

@@ -64,6 +64,10 @@ struct AttnDesc {
   const void* q = nullptr;      // [n][H][d] bf16
   void* o = nullptr;            // [n][H][d] bf16
   float* lse = nullptr;         // [H][n] or null
+  // active-row calls: only rows qrows[0 .. *qcount) of q / o / lse are
+  // computed (device memory; *qcount is clamped to [0, n]); null: all rows
+  const int32_t* qrows = nullptr;
+  const int32_t* qcount = nullptr;
   int n = 0;
   int heads = 0;
   int head_dim = 0;
@@ -76,10 +80,23 @@ struct AttnDesc {
   bool workspace_ready = false; // counters in the workspace already zeroed
 };
 
+// LiveEdit active-row mask (validated by the caller).
+struct EditMaskDesc {
+  const void* z_src = nullptr;  // [tokens][channels] bf16
+  const void* z_edit = nullptr;
+  int tokens = 0;               // 1..KVC_MAX_MASK_TOKENS
+  int channels = 0;
+  float tau = 0.f;              // threshold mode (keep < 0)
+  int keep = -1;                // top-k mode (keep >= 0)
+  int32_t* rows = nullptr;      // [tokens]
+  int32_t* count = nullptr;     // [1]
+};
+
 // Launchers.  Return KVC_OK or KVC_E_DEVICE / KVC_E_UNSUPPORTED.  The device
 // implementation lives in the HIP sources; tests link a recording fake.
 kvc_status launch_cache_write(const CacheWriteDesc& d, void* stream);
 kvc_status launch_attention(const AttnDesc& d, void* stream);
+kvc_status launch_edit_mask(const EditMaskDesc& d, void* stream);
 
 // Workspace bytes the attention launcher may use for a ring of this shape.
 size_t attention_workspace_bytes(int heads, int head_dim, int n, int kv_dtype);

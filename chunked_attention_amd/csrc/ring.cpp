@@ -216,6 +216,32 @@ int segment_table(const kvc_ring* r, kvc_segment* info, AttnSegment* dev) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+kvc_status attention_call(kvc_ring* r, const void* q, void* o, float* lse,
+                          const int32_t* rows, const int32_t* count, void* stream) {
+  if (!r || !q || !o || !aligned16(q) || !aligned16(o) || q == o) return KVC_E_INVAL;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return KVC_E_INVAL;
+  AttnDesc d;
+  d.qrows = rows;
+  d.qcount = count;
+  d.nseg = segment_table(r, nullptr, d.seg);
+  if (d.nseg < 0) return KVC_E_STATE;
+  d.q = q;
+  d.o = o;
+  d.lse = lse;
+  d.n = r->cfg.chunk_tokens + r->cfg.source_tokens;
+  d.heads = r->cfg.heads;
+  d.head_dim = r->cfg.head_dim;
+  d.kv_dtype = r->cfg.kv_dtype;
+  d.scale = r->scale;
+  d.workspace = r->base + r->L.work_off;
+  d.workspace_bytes = r->L.work_bytes;
+  d.workspace_ready = r->work_ready != 0;
+  kvc_status s = launch_attention(d, stream);
+  if (s == KVC_OK) r->work_ready = 1;
+  return s;
+}
 
 }  // namespace
 }  // namespace kvc
@@ -307,25 +333,34 @@ kvc_status kvc_append_chunk(kvc_ring* r, int32_t kind, const void* k, const void
 }
 
 kvc_status chunk_attn_fwd(kvc_ring* r, const void* q, void* o, float* lse, void* stream) {
-  if (!r || !q || !o || !aligned16(q) || !aligned16(o) || q == o) return KVC_E_INVAL;
-  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return KVC_E_INVAL;
-  AttnDesc d;
-  d.nseg = segment_table(r, nullptr, d.seg);
-  if (d.nseg < 0) return KVC_E_STATE;
-  d.q = q;
-  d.o = o;
-  d.lse = lse;
-  d.n = r->cfg.chunk_tokens + r->cfg.source_tokens;
-  d.heads = r->cfg.heads;
-  d.head_dim = r->cfg.head_dim;
-  d.kv_dtype = r->cfg.kv_dtype;
-  d.scale = r->scale;
-  d.workspace = r->base + r->L.work_off;
-  d.workspace_bytes = r->L.work_bytes;
-  d.workspace_ready = r->work_ready != 0;
-  kvc_status s = launch_attention(d, stream);
-  if (s == KVC_OK) r->work_ready = 1;
-  return s;
+  return attention_call(r, q, o, lse, nullptr, nullptr, stream);
+}
+
+kvc_status chunk_attn_fwd_rows(kvc_ring* r, const void* q, void* o, float* lse,
+                               const int32_t* rows, const int32_t* count, void* stream) {
+  if (!rows || !count || !aligned4(rows) || !aligned4(count)) return KVC_E_INVAL;
+  return attention_call(r, q, o, lse, rows, count, stream);
+}
+
+kvc_status kvc_edit_mask(const void* z_src, const void* z_edit, int32_t tokens, int32_t channels,
+                         float tau, int32_t keep, int32_t* rows, int32_t* count, void* stream) {
+  if (!z_src || !z_edit || !rows || !count) return KVC_E_INVAL;
+  if ((reinterpret_cast<uintptr_t>(z_src) & 1u) || (reinterpret_cast<uintptr_t>(z_edit) & 1u) ||
+      !aligned4(rows) || !aligned4(count))
+    return KVC_E_INVAL;
+  if (tokens < 1 || tokens > KVC_MAX_MASK_TOKENS) return KVC_E_INVAL;
+  if (channels < 1 || channels > KVC_MAX_MASK_CHANNELS) return KVC_E_INVAL;
+  if (keep < 0 && !(tau >= 0.f)) return KVC_E_INVAL;     // negative or NaN
+  EditMaskDesc d;
+  d.z_src = z_src;
+  d.z_edit = z_edit;
+  d.tokens = tokens;
+  d.channels = channels;
+  d.tau = tau;
+  d.keep = keep < 0 ? -1 : keep;
+  d.rows = rows;
+  d.count = count;
+  return launch_edit_mask(d, stream);
 }
 
 kvc_status kvc_evict(kvc_ring* r, int32_t* evicted) {

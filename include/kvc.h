@@ -79,6 +79,8 @@ typedef int32_t kvc_status;
 #define KVC_MAX_WINDOW   29       /* W <= 29 */
 #define KVC_MAX_SEGMENTS (KVC_MAX_WINDOW + 5)   /* cond, ref, sink, W window, current, source */
 #define KVC_TILE_KEYS    64       /* stored rows are padded to a multiple of this */
+#define KVC_MAX_MASK_TOKENS 16384 /* tokens of one kvc_edit_mask call */
+#define KVC_MAX_MASK_CHANNELS 4096
 #define KVC_ALIGN        256      /* dev_buf alignment */
 
 typedef struct kvc_config {
@@ -180,6 +182,57 @@ kvc_status kvc_append_chunk(kvc_ring* ring, int32_t kind, const void* k, const v
  * KVC_E_DEVICE.
  */
 kvc_status chunk_attn_fwd(kvc_ring* ring, const void* q, void* o, float* lse, void* stream);
+
+/*
+ * Attention of selected query rows only (LiveEdit's active rows).
+ * Source: aitrends.kr, "LiveEdit 실시간 Diffusion 기반 스트리밍 비디오 편집",
+ * AR-oriented Mask Cache (methodology and technical-detail sections): only
+ * the tokens whose mask is 1 are recomputed; the others reuse the previous
+ * chunk's cached features, here the rows of o left as they are.
+ *   q, o, lse  as for chunk_attn_fwd ([n+s][H][d], [H][n+s]); only rows
+ *              rows[0 .. *count) of q are read and of o / lse written; every
+ *              other row of o and lse keeps its contents.
+ *   rows       device int32 [n+s]: row indices, e.g. as written by
+ *              kvc_edit_mask.  Indices outside [0, n+s) are skipped; an index
+ *              listed twice is computed twice (same result).
+ *   count      device int32: number of entries of rows to use, clamped to
+ *              [0, n+s].  Read by the kernel, so it may be produced by an
+ *              earlier kernel on the stream without a host synchronisation.
+ * The result of each selected row is the one chunk_attn_fwd defines (up to
+ * rounding: the work split differs).  Errors as for chunk_attn_fwd, and
+ * KVC_E_INVAL for null or misaligned rows / count.
+ */
+kvc_status chunk_attn_fwd_rows(kvc_ring* ring, const void* q, void* o, float* lse,
+                               const int32_t* rows, const int32_t* count, void* stream);
+
+/*
+ * LiveEdit's active-row mask for the next chunk, on the device.
+ * Source: aitrends.kr, "LiveEdit 실시간 Diffusion 기반 스트리밍 비디오 편집",
+ * AR-oriented Mask Cache (methodology and technical-detail sections): a
+ * token is active where the L2 distance between the previous chunk's edited
+ * and source latents exceeds a threshold tau, chosen dynamically so that
+ * about 70% of the tokens are pruned.
+ *   z_src, z_edit  device bf16 [tokens][channels], token-major.
+ *   tokens         1 .. KVC_MAX_MASK_TOKENS;  channels 1 .. KVC_MAX_MASK_CHANNELS.
+ *   keep < 0       threshold mode: token i is active iff
+ *                    sum_c (z_edit[i][c] - z_src[i][c])^2  >  tau^2,
+ *                  the sum taken in float64 over c in increasing order, each
+ *                  difference, square and addition rounded on its own, and
+ *                  tau^2 = tau * tau in float64 (tau >= 0, not NaN).
+ *   keep >= 0      top-k mode (the dynamic threshold): the min(keep, tokens)
+ *                  tokens with the largest such sum are active; equal sums
+ *                  rank by lower index first.  tau is ignored.
+ *                  A NaN sum counts as -1 (never active unless needed to
+ *                  reach keep).
+ *   rows           device int32 [tokens]: the active token indices in
+ *                  increasing order, then -1 up to tokens.
+ *   count          device int32 [1]: the number of active tokens.
+ * Asynchronous on the stream; no host synchronisation, no allocation.
+ * Errors: KVC_E_INVAL (null or misaligned pointers, sizes out of range, bad
+ * tau in threshold mode), KVC_E_DEVICE.
+ */
+kvc_status kvc_edit_mask(const void* z_src, const void* z_edit, int32_t tokens, int32_t channels,
+                         float tau, int32_t keep, int32_t* rows, int32_t* count, void* stream);
 
 /*
  * Finish the current committed chunk and recycle cache memory (host only).

@@ -42,6 +42,8 @@ ROLES = {
     "v_src_clean": 11,
     "k_ref": 12,
     "v_ref": 13,
+    "z_src": 14,
+    "z_edit": 15,
 }
 
 
@@ -223,3 +225,32 @@ def zero_feature0(k: torch.Tensor) -> torch.Tensor:
     k = k.clone()
     k[..., 0] = 0.0
     return k
+
+
+def edit_latents(seed: int, chunk: int, grid: tuple[int, int], frames: int, channels: int,
+                 edit_frac: float = 0.3, background_std: float = 0.05):
+    """Synthetic (z_src, z_edit) latents of one chunk for LiveEdit's mask,
+    bf16 [frames * rows * cols, channels], token-major (frame, row, col).
+
+    z_src ~ N(0, 1).  z_edit = z_src plus small N(0, background_std^2) noise
+    everywhere (the preserved background) and N(0, 1) inside an edited
+    rectangle covering about ``edit_frac`` of each frame's grid, placed by the
+    seed (the edited object).  Only random draws: no distances, no masking.
+    """
+    rows, cols = grid
+    ss = np.random.SeedSequence([seed, 0, chunk, 0, ROLES["z_src"]])
+    rng = np.random.default_rng(ss)
+    z_src = rng.standard_normal((frames, rows, cols, channels), dtype=np.float32)
+    ss = np.random.SeedSequence([seed, 0, chunk, 0, ROLES["z_edit"]])
+    rng = np.random.default_rng(ss)
+    noise = rng.standard_normal((frames, rows, cols, channels), dtype=np.float32)
+    delta = noise * np.float32(background_std)
+    side = math.sqrt(edit_frac)
+    h, w = max(1, round(rows * side)), max(1, round(cols * side))
+    r0 = int(rng.integers(0, rows - h + 1))
+    c0 = int(rng.integers(0, cols - w + 1))
+    delta[:, r0:r0 + h, c0:c0 + w, :] = noise[:, r0:r0 + h, c0:c0 + w, :]
+    z_edit = z_src + delta
+    flat = (frames * rows * cols, channels)
+    return (torch.from_numpy(z_src.reshape(flat)).to(torch.bfloat16),
+            torch.from_numpy(z_edit.reshape(flat)).to(torch.bfloat16))

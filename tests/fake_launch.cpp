@@ -15,7 +15,10 @@
 namespace {
 
 struct Record {
-  int32_t kind;       // 0 cache write, 1 attention
+  int32_t kind;       // 0 cache write, 1 attention, 2 edit mask
+                      // (mask: rows = tokens, pitch = channels, nseg = keep,
+                      // scale = tau, src_k/src_v = z_src/z_edit,
+                      // dst_k/dst_vt = rows/count)
   int32_t rows;       // write: rows; attention: n
   int32_t pitch;      // write: pitch
   int32_t nseg;       // attention
@@ -30,6 +33,8 @@ struct Record {
   int32_t kv_dtype;
   uint64_t k_scale;   // write (fp8)
   uint64_t stream;
+  uint64_t qrows;     // attention: active-row map (0: all rows)
+  uint64_t qcount;    // attention: active-row count
 };
 
 std::vector<Record> g_log;
@@ -79,6 +84,26 @@ kvc_status launch_attention(const AttnDesc& d, void* stream) {
   }
   r.scale = d.scale;
   r.kv_dtype = d.kv_dtype;
+  r.stream = reinterpret_cast<uint64_t>(stream);
+  r.qrows = reinterpret_cast<uint64_t>(d.qrows);
+  r.qcount = reinterpret_cast<uint64_t>(d.qcount);
+  g_log.push_back(r);
+  return KVC_OK;
+}
+
+kvc_status launch_edit_mask(const EditMaskDesc& d, void* stream) {
+  if (kvc_status s = take_failure()) return s;
+  Record r;
+  std::memset(&r, 0, sizeof(r));
+  r.kind = 2;
+  r.rows = d.tokens;
+  r.pitch = d.channels;
+  r.nseg = d.keep;
+  r.scale = d.tau;
+  r.src_k = reinterpret_cast<uint64_t>(d.z_src);
+  r.src_v = reinterpret_cast<uint64_t>(d.z_edit);
+  r.dst_k = reinterpret_cast<uint64_t>(d.rows);
+  r.dst_vt = reinterpret_cast<uint64_t>(d.count);
   r.stream = reinterpret_cast<uint64_t>(stream);
   g_log.push_back(r);
   return KVC_OK;

@@ -27,7 +27,8 @@ class Record(ctypes.Structure):
                 ("seg_rows", ctypes.c_int32 * kv.KVC_MAX_SEGMENTS),
                 ("seg_pitch", ctypes.c_int32 * kv.KVC_MAX_SEGMENTS),
                 ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
-                ("k_scale", ctypes.c_uint64), ("stream", ctypes.c_uint64)]
+                ("k_scale", ctypes.c_uint64), ("stream", ctypes.c_uint64),
+                ("qrows", ctypes.c_uint64), ("qcount", ctypes.c_uint64)]
 
 
 @pytest.fixture(scope="module")
