@@ -33,6 +33,7 @@ Modules:
   brute      -- O2: whole-stream attention under a block-causal window mask.
   fp8        -- O3: OCP e4m3 codec and the per-(head, segment) scale rule.
   liveedit   -- O4: LiveEdit's active-row mask and active-row attention.
+  rope       -- O5: rotary encoding of Q and K from a per-token angle table.
 
 Readings where the pages are silent (each is listed in the design notes):
   * W counts past chunks only; the sink and the current chunk come on top.
@@ -48,4 +49,4 @@ tests/test_fp8_codec.py (brute force, closed forms, library routines,
 invariants).  None is "parity unpinned".
 """
 
-from . import attention, brute, fp8, liveedit  # noqa: F401
+from . import attention, brute, fp8, liveedit, rope  # noqa: F401
