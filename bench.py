@@ -115,7 +115,8 @@ def _cpu_model() -> str:
 class Inputs:
     """Per-chunk inputs uploaded once (a pool of `pool` chunk sets)."""
 
-    def __init__(self, w, pool: int, dist: str, device, active_rows: bool = False):
+    def __init__(self, w, pool: int, dist: str, device, active_rows: bool = False,
+                 rope: bool = False):
         import torch
         import synth
         s = synth.Stream(w, dist)
@@ -142,6 +143,12 @@ class Inputs:
             self.noisy.append(noisy)
             self.clean.append((up(k, sk), up(v, sv)))
         self.pool = pool
+        # rotary encoding: one angle table per chunk for K and one for Q
+        nq = w.chunk_tokens + w.source_tokens
+        self.rope_k = [synth.rope_table(w.seed, c, nq, w.head_dim).to(device) if rope else None
+                       for c in range(pool)]
+        self.rope_q = [synth.rope_table(w.seed, 1000 + c, nq, w.head_dim).to(device)
+                       if rope else None for c in range(pool)]
         # LiveEdit: the previous chunk's (source, edited) latents, 16 channels
         self.latents = []
         if active_rows:
@@ -162,7 +169,8 @@ def run_stream_bench(w, args, device, flat: bool):
     import chunked_attention_amd as kv
 
     pool = min(args.pool, w.chunks) if args.pool else w.chunks
-    inp = Inputs(w, pool, args.dist, device, active_rows=args.active_rows is not None)
+    inp = Inputs(w, pool, args.dist, device, active_rows=args.active_rows is not None,
+                 rope=args.rope)
     keep = active_keep(w, args.active_rows) if args.active_rows is not None else None
     nq = w.chunk_tokens + w.source_tokens
     rows_buf = torch.empty(nq, dtype=torch.int32, device=device)
@@ -214,16 +222,16 @@ def run_stream_bench(w, args, device, flat: bool):
 
         def attend(r, q, out):
             if keep is None:
-                r.attention(q, out=out)
+                r.attention(q, out=out, rope=inp.rope_q[c])
             else:
-                r.attention_rows(q, rows_buf, count_buf, out=out)
+                r.attention_rows(q, rows_buf, count_buf, out=out, rope=inp.rope_q[c])
 
         for st in range(w.steps):
             for li, r in enumerate(rings):
                 if timed:
                     e0, e1, e2 = next(ev_iter), next(ev_iter), next(ev_iter)
                     e0.record(stream)
-                    r.stage(*inp.noisy[c][st])
+                    r.stage(*inp.noisy[c][st], rope=inp.rope_k[c])
                     e1.record(stream)
                     attend(r, inp.q[c][st], outs[li & 1])
                     e2.record(stream)
@@ -232,13 +240,13 @@ def run_stream_bench(w, args, device, flat: bool):
                     write_events.append((e0, e1))
                     attn_events.append((e1, e2))
                 else:
-                    r.stage(*inp.noisy[c][st])
+                    r.stage(*inp.noisy[c][st], rope=inp.rope_k[c])
                     attend(r, inp.q[c][st], outs[li & 1])
         for li, r in enumerate(rings):
             if timed:
                 e0, e1 = next(ev_iter), next(ev_iter)
                 e0.record(stream)
-                r.commit(*inp.clean[c])
+                r.commit(*inp.clean[c], rope=inp.rope_k[c])
                 e1.record(stream)
                 write_events.append((e0, e1))
                 if args.clean_pass:
@@ -250,7 +258,7 @@ def run_stream_bench(w, args, device, flat: bool):
                     e2.record(stream)
                     attn_events.append((e1, e2))
             else:
-                r.commit(*inp.clean[c])
+                r.commit(*inp.clean[c], rope=inp.rope_k[c])
                 if args.clean_pass:
                     attend(r, inp.q[c][0], outs[li & 1])
             r.evict()
@@ -425,6 +433,9 @@ def main() -> int:
     ap.add_argument("--active-rows", type=float, default=None, metavar="FRAC",
                     help="LiveEdit: each chunk attends only the top FRAC of its rows by the "
                          "edit distance of the previous chunk's latents (mask on the device)")
+    ap.add_argument("--rope", action="store_true",
+                    help="rotary encoding fused into the cache writes and the Q load "
+                         "(one angle table per chunk)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -497,6 +508,7 @@ def main() -> int:
                         f"m={w.cond_tokens} r={w.ref_tokens} s={w.source_tokens} "
                         f"W={w.window} layers={w.layers} steps={w.steps}"
                         f"{' +clean pass' if args.clean_pass else ''}"
+                        f"{' +fused rope' if args.rope else ''}"
                         f"{f' active rows {queries} (top-k edit mask)' if queries is not None else ''}, "
                         f"steady-state chunks {r['first_chunk']}..{r['last_chunk']} "
                         f"(|S|={r['kv_len']} keys); one step = STAGE + attention per "
@@ -507,6 +519,7 @@ def main() -> int:
             "ref_tokens": w.ref_tokens, "source_tokens": w.source_tokens,
             "clean_pass": args.clean_pass,
             "active_rows": queries,
+            "rope": args.rope,
         },
         "chunks_per_s": round(1.0 / step_s, 2),
         "pct_mfma_peak": round(100 * value / peak, 2),
@@ -527,8 +540,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": f"attn_fwd_bf16<{w.head_dim},false>" if not fp8 else
-                      f"attn_fwd_fp8<{w.head_dim},false>",
+            "kernel": f"attn_fwd_{'fp8' if fp8 else 'bf16'}<{w.head_dim},false,"
+                      f"{'true' if args.rope else 'false'}>",
             "per_launch_flops": flops,
         },
     }

@@ -73,7 +73,7 @@ class kvc_slot_view(ctypes.Structure):
 EXPORTS = (
     "kvc_required_bytes", "kvc_create", "kvc_append_chunk", "chunk_attn_fwd", "kvc_evict",
     "kvc_destroy", "kvc_status_str", "kvc_get_info", "kvc_get_segments", "kvc_get_slot",
-    "chunk_attn_fwd_rows", "kvc_edit_mask",
+    "chunk_attn_fwd_rows", "kvc_edit_mask", "kvc_append_chunk_rope", "chunk_attn_fwd_rope",
 )
 
 
@@ -94,6 +94,10 @@ def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.chunk_attn_fwd_rows.restype = I
     lib.kvc_edit_mask.argtypes = [P, P, I, I, ctypes.c_float, I, P, P, P]
     lib.kvc_edit_mask.restype = I
+    lib.kvc_append_chunk_rope.argtypes = [P, I, P, P, P, P]
+    lib.kvc_append_chunk_rope.restype = I
+    lib.chunk_attn_fwd_rope.argtypes = [P, P, P, P, P, P, P, P]
+    lib.chunk_attn_fwd_rope.restype = I
     lib.kvc_evict.argtypes = [P, ctypes.POINTER(I)]
     lib.kvc_evict.restype = I
     lib.kvc_destroy.argtypes = [P]
@@ -182,13 +186,31 @@ def _check_tokens(x, rows: int, cfg: kvc_config, what: str) -> None:
                          f"{(rows, cfg.heads, cfg.head_dim)}")
 
 
-def kvc_append_chunk(handle, cfg: kvc_config, kind: int, k, v, stream=None) -> None:
+def _check_rope(rope, rows: int, cfg: kvc_config) -> ctypes.c_void_p:
+    import torch
+    if rope is None:
+        return ctypes.c_void_p(None)
+    if rope.dtype != torch.float32 or not rope.is_cuda or not rope.is_contiguous() or \
+            tuple(rope.shape) != (rows, cfg.head_dim // 2, 2):
+        raise ValueError(f"rope must be a contiguous float32 CUDA tensor "
+                         f"[{rows}, {cfg.head_dim // 2}, 2]")
+    return ctypes.c_void_p(rope.data_ptr())
+
+
+def kvc_append_chunk(handle, cfg: kvc_config, kind: int, k, v, stream=None, rope=None) -> None:
+    """Cache write; with `rope` (float32 [rows, d/2, 2] of (cos, sin)) the
+    keys are stored rotated (kvc_append_chunk_rope)."""
     rows = {KVC_COND: cfg.cond_tokens, KVC_REF: cfg.ref_tokens}.get(kind, query_rows(cfg))
     _check_tokens(k, rows, cfg, "k")
     _check_tokens(v, rows, cfg, "v")
-    _check(lib().kvc_append_chunk(handle, kind, ctypes.c_void_p(k.data_ptr()),
-                                  ctypes.c_void_p(v.data_ptr()), _stream_handle(stream)),
-           "kvc_append_chunk")
+    if rope is None:
+        st = lib().kvc_append_chunk(handle, kind, ctypes.c_void_p(k.data_ptr()),
+                                    ctypes.c_void_p(v.data_ptr()), _stream_handle(stream))
+    else:
+        st = lib().kvc_append_chunk_rope(handle, kind, ctypes.c_void_p(k.data_ptr()),
+                                         ctypes.c_void_p(v.data_ptr()),
+                                         _check_rope(rope, rows, cfg), _stream_handle(stream))
+    _check(st, "kvc_append_chunk")
 
 
 def _attn_args(cfg: kvc_config, q, o, lse):
@@ -229,6 +251,22 @@ def chunk_attn_fwd_rows(handle, cfg: kvc_config, q, o, rows, count, lse=None,
                                      ctypes.c_void_p(rows.data_ptr()),
                                      ctypes.c_void_p(count.data_ptr()),
                                      _stream_handle(stream)), "chunk_attn_fwd_rows")
+
+
+def chunk_attn_fwd_rope(handle, cfg: kvc_config, q, o, rope, lse=None, rows=None, count=None,
+                        stream=None) -> None:
+    """Attention with q rotated by `rope` (float32 [n+s, d/2, 2]) as it is
+    loaded; rows/count optionally select active rows."""
+    if (rows is None) != (count is None):
+        raise ValueError("give both rows and count, or neither")
+    rp = rc = ctypes.c_void_p(None)
+    if rows is not None:
+        _check_i32(rows, "rows", query_rows(cfg))
+        _check_i32(count, "count", 1)
+        rp, rc = ctypes.c_void_p(rows.data_ptr()), ctypes.c_void_p(count.data_ptr())
+    _check(lib().chunk_attn_fwd_rope(handle, *_attn_args(cfg, q, o, lse),
+                                     _check_rope(rope, query_rows(cfg), cfg), rp, rc,
+                                     _stream_handle(stream)), "chunk_attn_fwd_rope")
 
 
 def kvc_edit_mask(z_src, z_edit, tau: float | None = None, keep: int | None = None, rows=None,
@@ -316,28 +354,34 @@ class Ring:
         except Exception:
             pass
 
-    def cond(self, k, v, stream=None) -> None:
-        kvc_append_chunk(self.handle, self.cfg, KVC_COND, k, v, stream)
+    def cond(self, k, v, stream=None, rope=None) -> None:
+        kvc_append_chunk(self.handle, self.cfg, KVC_COND, k, v, stream, rope)
 
-    def ref(self, k, v, stream=None) -> None:
-        kvc_append_chunk(self.handle, self.cfg, KVC_REF, k, v, stream)
+    def ref(self, k, v, stream=None, rope=None) -> None:
+        kvc_append_chunk(self.handle, self.cfg, KVC_REF, k, v, stream, rope)
 
-    def stage(self, k, v, stream=None) -> None:
-        kvc_append_chunk(self.handle, self.cfg, KVC_STAGE, k, v, stream)
+    def stage(self, k, v, stream=None, rope=None) -> None:
+        kvc_append_chunk(self.handle, self.cfg, KVC_STAGE, k, v, stream, rope)
 
-    def commit(self, k, v, stream=None) -> None:
-        kvc_append_chunk(self.handle, self.cfg, KVC_COMMIT, k, v, stream)
+    def commit(self, k, v, stream=None, rope=None) -> None:
+        kvc_append_chunk(self.handle, self.cfg, KVC_COMMIT, k, v, stream, rope)
 
-    def attention(self, q, out=None, lse=None, stream=None):
+    def attention(self, q, out=None, lse=None, stream=None, rope=None):
         import torch
         if out is None:
             out = torch.empty_like(q)
-        chunk_attn_fwd(self.handle, self.cfg, q, out, lse, stream)
+        if rope is None:
+            chunk_attn_fwd(self.handle, self.cfg, q, out, lse, stream)
+        else:
+            chunk_attn_fwd_rope(self.handle, self.cfg, q, out, rope, lse, stream=stream)
         return out
 
-    def attention_rows(self, q, rows, count, out, lse=None, stream=None):
+    def attention_rows(self, q, rows, count, out, lse=None, stream=None, rope=None):
         """Active-row attention: only rows[:count] of `out` are written."""
-        chunk_attn_fwd_rows(self.handle, self.cfg, q, out, rows, count, lse, stream)
+        if rope is None:
+            chunk_attn_fwd_rows(self.handle, self.cfg, q, out, rows, count, lse, stream)
+        else:
+            chunk_attn_fwd_rope(self.handle, self.cfg, q, out, rope, lse, rows, count, stream)
         return out
 
     def evict(self) -> int:

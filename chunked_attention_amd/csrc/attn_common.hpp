@@ -50,6 +50,7 @@ struct AttnArgs {
   float* lse;
   const int* qrows;         // active-row calls: query i is row qrows[i] of q / o / lse
   const int* qcount;        // active-row calls: number of active rows (device memory)
+  const float* qrope;       // optional rotation of q rows: [ld][D/2][(cos, sin)]
   float* part_o;            // [2*nwg][kBq*D] partial O, accumulator layout
   float* part_ml;           // [2*nwg][waves][3][32] partial reference, sum, exact sum
   unsigned* counters;       // [nrows][2]: arrived, partials written

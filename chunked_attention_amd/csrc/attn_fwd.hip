@@ -72,7 +72,7 @@ struct Geo {
   static_assert(kKInstr >= 1 && kVInstr >= 1 && kKInstr == kVInstr, "copy counts");
 };
 
-template <int D, bool kLse>
+template <int D, bool kLse, bool kRope>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(const AttnArgs a) {
   using G = Geo<D>;
@@ -206,7 +206,10 @@ void attn_fwd_bf16(const AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < kDS; ++ks) {
         if (g >= 0) {
-          qreg[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
+          uint4 u = ld16(qrow + ks * 16);
+          if constexpr (kRope)
+            u = rope8(u, a.qrope + (static_cast<size_t>(g) * (D / 2) + ks * 8 + half * 4) * 2);
+          qreg[ks] = __builtin_bit_cast(bf16x8_t, u);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) qreg[ks][j] = static_cast<__bf16>(0.0f);
@@ -389,10 +392,14 @@ kvc_status launch_bf16(const AttnDesc& d, hipStream_t stream) {
   const kvc_status st = fill_args(d, Geo<D>::kStep, a);
   if (st != KVC_OK) return st;
   if (!d.workspace_ready) launch_fill_u32(a.counters, 2 * a.nrows, 0u, stream);
-  if (a.lse)
-    hipLaunchKernelGGL((attn_fwd_bf16<D, true>), dim3(a.nwg), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_fwd_bf16<D, false>), dim3(a.nwg), dim3(kThreads), 0, stream, a);
+  const dim3 grid(a.nwg), block(kThreads);
+  if (a.qrope) {
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16<D, false, true>), grid, block, 0, stream, a);
+  } else {
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16<D, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_DEVICE;
 }
 
@@ -427,6 +434,7 @@ kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a) {
   a.lse = d.lse;
   a.qrows = d.qrows;
   a.qcount = d.qcount;
+  a.qrope = d.qrope;
   a.n = d.n;
   a.ld = d.n;
   a.heads = d.heads;

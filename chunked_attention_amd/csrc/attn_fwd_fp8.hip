@@ -87,7 +87,7 @@ __device__ __forceinline__ int pack8(float x, float y, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(x, y, old, kHigh);
 }
 
-template <int D, bool kLse>
+template <int D, bool kLse, bool kRope>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8(const AttnArgs a) {
   using G = Geo8<D>;
@@ -228,7 +228,12 @@ void attn_fwd_fp8(const AttnArgs a) {
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           uint4 u = make_uint4(0, 0, 0, 0);
-          if (g >= 0) u = ld16(qrow + ks * 64 + c4 * 8);
+          if (g >= 0) {
+            u = ld16(qrow + ks * 64 + c4 * 8);
+            if constexpr (kRope)
+              u = rope8(u, a.qrope + (static_cast<size_t>(g) * (D / 2) + ks * 32 + half * 16 +
+                                      c4 * 4) * 2);
+          }
           const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -433,10 +438,14 @@ kvc_status launch_fp8_d(const AttnDesc& d, hipStream_t stream) {
   for (int s = 0; s < a.nseg; ++s)
     if (!a.seg[s].ks || !a.seg[s].vs) return KVC_E_INVAL;
   if (!d.workspace_ready) launch_fill_u32(a.counters, 2 * a.nrows, 0u, stream);
-  if (a.lse)
-    hipLaunchKernelGGL((attn_fwd_fp8<D, true>), dim3(a.nwg), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_fwd_fp8<D, false>), dim3(a.nwg), dim3(kThreads), 0, stream, a);
+  const dim3 grid(a.nwg), block(kThreads);
+  if (a.qrope) {
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_fp8<D, false, true>), grid, block, 0, stream, a);
+  } else {
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_fp8<D, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_DEVICE;
 }
 

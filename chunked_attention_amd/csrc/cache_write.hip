@@ -14,6 +14,11 @@
 // deployment section: after generation the clean KV is cached; the pages'
 // per-chunk table lists this save step as its own stage).
 //
+// With a rotation table the keys are stored rotary-encoded (the fused M-RoPE
+// of the same page's architecture section; the angles come from the caller,
+// the rounding is that of rope8: float32 then bf16).  fp8 rings quantise the
+// rotated keys, their scale taken over the rotated values.
+//
 // HBM-bound: each element is read once and written once.  One workgroup
 // handles 64 rows of one head; V goes through LDS for the transpose.
 #include "device_common.hpp"
@@ -42,7 +47,8 @@ __device__ __forceinline__ int pi64(int p) {
 template <int D>
 __global__ __launch_bounds__(kThreads) void cache_write_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int rows, int pitch,
-    int heads, uint16_t* __restrict__ kd, uint16_t* __restrict__ vtd) {
+    int heads, uint16_t* __restrict__ kd, uint16_t* __restrict__ vtd,
+    const float* __restrict__ rope) {
   constexpr int kChunks = D / 8;         // 16-byte chunks per row
   constexpr int kLdsPitch = D + 2;       // u16 per LDS row; odd word count avoids conflicts
   __shared__ uint32_t vtile32[kRowsPerBlock * kLdsPitch / 2];
@@ -61,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_bf16(
       const size_t src = (static_cast<size_t>(r) * heads + h) * D + ch * 8;
       kv = ld16(k + src);
       vv = ld16(v + src);
+      if (rope) kv = rope8(kv, rope + (static_cast<size_t>(r) * (D / 2) + ch * 4) * 2);
     }
     st16(kd + (static_cast<size_t>(h) * pitch + r) * D + ch * 8, kv);
     uint32_t* dst = reinterpret_cast<uint32_t*>(vtile + row * kLdsPitch + ch * 8);
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void cache_write_bf16(
 template <int D>
 __global__ __launch_bounds__(kThreads) void cache_amax_fp8(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int rows, int heads,
-    float* __restrict__ partial /* [2][H][nblk] */) {
+    float* __restrict__ partial /* [2][H][nblk] */, const float* __restrict__ rope) {
   constexpr int kChunks = D / 8;
   __shared__ float red[2][kThreads / 64];
   const int h = blockIdx.y;
@@ -104,8 +111,9 @@ __global__ __launch_bounds__(kThreads) void cache_amax_fp8(
     const int r = r0 + c / kChunks;
     if (r >= rows) break;
     const size_t src = (static_cast<size_t>(r) * heads + h) * D + (c % kChunks) * 8;
-    const uint4 kv = ld16(k + src);
+    uint4 kv = ld16(k + src);
     const uint4 vv = ld16(v + src);
+    if (rope) kv = rope8(kv, rope + (static_cast<size_t>(r) * (D / 2) + (c % kChunks) * 4) * 2);
     const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
     const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -144,7 +152,8 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int rows, int pitch,
     int heads, int nblk_rows, const float* __restrict__ partial, uint8_t* __restrict__ kd,
-    uint8_t* __restrict__ vtd, float* __restrict__ k_scale, float* __restrict__ v_scale) {
+    uint8_t* __restrict__ vtd, float* __restrict__ k_scale, float* __restrict__ v_scale,
+    const float* __restrict__ rope) {
   constexpr int kChunks = D / 8;         // 8-element chunks per row
   constexpr int kLdsPitch = D + 4;       // bytes per LDS row of codes
   __shared__ __attribute__((aligned(16))) uint8_t vtile[kRowsPerBlock * kLdsPitch];
@@ -185,8 +194,9 @@ __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
     uint32_t kc[2] = {0u, 0u}, vc[2] = {0u, 0u};
     if (r < rows) {
       const size_t src = (static_cast<size_t>(r) * heads + h) * D + ch * 8;
-      const uint4 kv = ld16(k + src);
+      uint4 kv = ld16(k + src);
       const uint4 vv = ld16(v + src);
+      if (rope) kv = rope8(kv, rope + (static_cast<size_t>(r) * (D / 2) + ch * 4) * 2);
       const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
       const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -233,17 +243,17 @@ kvc_status launch_write(const CacheWriteDesc& d, hipStream_t s) {
     hipLaunchKernelGGL(cache_write_bf16<D>, grid, block, 0, s,
                        static_cast<const uint16_t*>(d.k), static_cast<const uint16_t*>(d.v),
                        d.rows, d.pitch, d.heads, static_cast<uint16_t*>(d.k_dst),
-                       static_cast<uint16_t*>(d.vt_dst));
+                       static_cast<uint16_t*>(d.vt_dst), d.rope);
   } else {
     const int nblk = (d.rows + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(cache_amax_fp8<D>, dim3(nblk, d.heads), block, 0, s,
                        static_cast<const uint16_t*>(d.k), static_cast<const uint16_t*>(d.v),
-                       d.rows, d.heads, d.scratch);
+                       d.rows, d.heads, d.scratch, d.rope);
     hipLaunchKernelGGL(cache_quant_fp8<D>, grid, block, 0, s,
                        static_cast<const uint16_t*>(d.k), static_cast<const uint16_t*>(d.v),
                        d.rows, d.pitch, d.heads, nblk, d.scratch,
                        static_cast<uint8_t*>(d.k_dst), static_cast<uint8_t*>(d.vt_dst),
-                       d.k_scale, d.v_scale);
+                       d.k_scale, d.v_scale, d.rope);
   }
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_DEVICE;
 }

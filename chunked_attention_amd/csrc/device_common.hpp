@@ -38,6 +38,34 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
+// Rotary encoding of one 16-byte chunk of bf16 features (pairs p .. p+3 of a
+// token) by the angles of a float32 table row: t = (cos, sin) of the four
+// pairs.  x' = x cos - y sin, y' = x sin + y cos, each product and the
+// sum/difference rounded to float32 on its own (no fused multiply-add), then
+// rounded to bf16 (nearest, ties to even).
+__device__ __forceinline__ uint4 rope8(uint4 x, const float* __restrict__ t) {
+#pragma clang fp contract(off)
+  const float4 t0 = *reinterpret_cast<const float4*>(t);
+  const float4 t1 = *reinterpret_cast<const float4*>(t + 4);
+  const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+  uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float xe = bf16_bits_to_float(w[p] & 0xFFFFu);
+    const float xo = bf16_bits_to_float(w[p] >> 16);
+    const float c = cs[2 * p], s = cs[2 * p + 1];
+    // plain operators under contract(off): HIP's __fmul_rn is a plain
+    // multiply defined outside this pragma, which the compiler would fuse
+    const float ec = xe * c, os = xo * s, es = xe * s, oc = xo * c;
+    const float re = ec - os;
+    const float ro = es + oc;
+    const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(re));
+    const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(ro));
+    w[p] = lo | (hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {

@@ -48,6 +48,7 @@ struct CacheWriteDesc {
   float* k_scale = nullptr;    // [H] (fp8)
   float* v_scale = nullptr;    // [H] (fp8)
   float* scratch = nullptr;    // fp8: float32 [2][H][pitch/kTileKeys] partial amax
+  const float* rope = nullptr; // optional rotation of K: float32 [rows][d/2][(cos, sin)]
 };
 
 // One logical segment of the visible KV, in device terms.
@@ -68,6 +69,7 @@ struct AttnDesc {
   // computed (device memory; *qcount is clamped to [0, n]); null: all rows
   const int32_t* qrows = nullptr;
   const int32_t* qcount = nullptr;
+  const float* qrope = nullptr;  // optional rotation of q: float32 [n][d/2][(cos, sin)]
   int n = 0;
   int heads = 0;
   int head_dim = 0;

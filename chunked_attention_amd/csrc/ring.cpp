@@ -135,8 +135,10 @@ int free_slot(const kvc_ring* r) {
   return -1;
 }
 
-CacheWriteDesc write_desc(const kvc_ring* r, const SlotGeom& g, const void* k, const void* v) {
+CacheWriteDesc write_desc(const kvc_ring* r, const SlotGeom& g, const void* k, const void* v,
+                          const float* rope) {
   CacheWriteDesc d;
+  d.rope = rope;
   d.k = k;
   d.v = v;
   d.rows = g.rows;
@@ -218,13 +220,15 @@ int segment_table(const kvc_ring* r, kvc_segment* info, AttnSegment* dev) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-kvc_status attention_call(kvc_ring* r, const void* q, void* o, float* lse,
+kvc_status attention_call(kvc_ring* r, const void* q, void* o, float* lse, const float* rope,
                           const int32_t* rows, const int32_t* count, void* stream) {
   if (!r || !q || !o || !aligned16(q) || !aligned16(o) || q == o) return KVC_E_INVAL;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return KVC_E_INVAL;
+  if (rope && !aligned16(rope)) return KVC_E_INVAL;
   AttnDesc d;
   d.qrows = rows;
   d.qcount = count;
+  d.qrope = rope;
   d.nseg = segment_table(r, nullptr, d.seg);
   if (d.nseg < 0) return KVC_E_STATE;
   d.q = q;
@@ -241,6 +245,61 @@ kvc_status attention_call(kvc_ring* r, const void* q, void* o, float* lse,
   kvc_status s = launch_attention(d, stream);
   if (s == KVC_OK) r->work_ready = 1;
   return s;
+}
+
+kvc_status append(kvc_ring* r, int32_t kind, const void* k, const void* v, const float* rope,
+                  void* stream) {
+  if (!r || !k || !v || !aligned16(k) || !aligned16(v)) return KVC_E_INVAL;
+  if (rope && !aligned16(rope)) return KVC_E_INVAL;
+  if (kind == KVC_COND) {
+    if (r->cfg.cond_tokens <= 0) return KVC_E_INVAL;
+    kvc_status s = launch_cache_write(write_desc(r, r->L.cond, k, v, rope), stream);
+    if (s != KVC_OK) return s;
+    r->cond_valid = 1;
+    return KVC_OK;
+  }
+  if (kind == KVC_REF) {
+    if (r->cfg.ref_tokens <= 0) return KVC_E_INVAL;
+    kvc_status s = launch_cache_write(write_desc(r, r->L.ref, k, v, rope), stream);
+    if (s != KVC_OK) return s;
+    r->ref_valid = 1;
+    return KVC_OK;
+  }
+  if (kind != KVC_STAGE && kind != KVC_COMMIT) return KVC_E_INVAL;
+  if (r->phase == KVC_PHASE_COMMITTED) return KVC_E_STATE;
+  int slot = r->phase == KVC_PHASE_STAGED ? r->staging : free_slot(r);
+  if (slot < 0) return KVC_E_STATE;
+  kvc_status s = launch_cache_write(write_desc(r, r->L.chunk[slot], k, v, rope), stream);
+  if (s != KVC_OK) return s;
+  if (r->cfg.source_tokens > 0) {
+    // rows n.. of the caller's tensors (and of the rotation table) are the
+    // chunk's source tokens
+    const size_t n = static_cast<size_t>(r->cfg.chunk_tokens);
+    const size_t skip = n * r->cfg.heads * r->cfg.head_dim * 2;
+    s = launch_cache_write(write_desc(r, r->L.source, static_cast<const char*>(k) + skip,
+                                      static_cast<const char*>(v) + skip,
+                                      rope ? rope + n * r->cfg.head_dim : nullptr),
+                           stream);
+    if (s != KVC_OK) return s;
+  }
+  r->current = slot;
+  if (kind == KVC_STAGE) {
+    r->staging = slot;
+    r->phase = KVC_PHASE_STAGED;
+    return KVC_OK;
+  }
+  // COMMIT: publish as the sink (chunk 0) or the newest window chunk
+  r->slot_chunk[slot] = r->t;
+  if (r->t == 0) {
+    r->sink_slot = slot;
+  } else {
+    r->win_id[r->n_win] = r->t;
+    r->win_slot[r->n_win] = slot;
+    ++r->n_win;
+  }
+  r->staging = -1;
+  r->phase = KVC_PHASE_COMMITTED;
+  return KVC_OK;
 }
 
 }  // namespace
@@ -281,65 +340,32 @@ kvc_status kvc_create(const kvc_config* cfg, void* dev_buf, size_t bytes, kvc_ri
   return KVC_OK;
 }
 
-kvc_status kvc_append_chunk(kvc_ring* r, int32_t kind, const void* k, const void* v,
-                            void* stream) {
-  if (!r || !k || !v || !aligned16(k) || !aligned16(v)) return KVC_E_INVAL;
-  if (kind == KVC_COND) {
-    if (r->cfg.cond_tokens <= 0) return KVC_E_INVAL;
-    kvc_status s = launch_cache_write(write_desc(r, r->L.cond, k, v), stream);
-    if (s != KVC_OK) return s;
-    r->cond_valid = 1;
-    return KVC_OK;
-  }
-  if (kind == KVC_REF) {
-    if (r->cfg.ref_tokens <= 0) return KVC_E_INVAL;
-    kvc_status s = launch_cache_write(write_desc(r, r->L.ref, k, v), stream);
-    if (s != KVC_OK) return s;
-    r->ref_valid = 1;
-    return KVC_OK;
-  }
-  if (kind != KVC_STAGE && kind != KVC_COMMIT) return KVC_E_INVAL;
-  if (r->phase == KVC_PHASE_COMMITTED) return KVC_E_STATE;
-  int slot = r->phase == KVC_PHASE_STAGED ? r->staging : free_slot(r);
-  if (slot < 0) return KVC_E_STATE;
-  kvc_status s = launch_cache_write(write_desc(r, r->L.chunk[slot], k, v), stream);
-  if (s != KVC_OK) return s;
-  if (r->cfg.source_tokens > 0) {
-    // rows n.. of the caller's tensors are the chunk's source tokens
-    const size_t skip = static_cast<size_t>(r->cfg.chunk_tokens) * r->cfg.heads *
-                        r->cfg.head_dim * 2;
-    s = launch_cache_write(write_desc(r, r->L.source, static_cast<const char*>(k) + skip,
-                                      static_cast<const char*>(v) + skip), stream);
-    if (s != KVC_OK) return s;
-  }
-  r->current = slot;
-  if (kind == KVC_STAGE) {
-    r->staging = slot;
-    r->phase = KVC_PHASE_STAGED;
-    return KVC_OK;
-  }
-  // COMMIT: publish as the sink (chunk 0) or the newest window chunk
-  r->slot_chunk[slot] = r->t;
-  if (r->t == 0) {
-    r->sink_slot = slot;
-  } else {
-    r->win_id[r->n_win] = r->t;
-    r->win_slot[r->n_win] = slot;
-    ++r->n_win;
-  }
-  r->staging = -1;
-  r->phase = KVC_PHASE_COMMITTED;
-  return KVC_OK;
-}
-
 kvc_status chunk_attn_fwd(kvc_ring* r, const void* q, void* o, float* lse, void* stream) {
-  return attention_call(r, q, o, lse, nullptr, nullptr, stream);
+  return attention_call(r, q, o, lse, nullptr, nullptr, nullptr, stream);
 }
 
 kvc_status chunk_attn_fwd_rows(kvc_ring* r, const void* q, void* o, float* lse,
                                const int32_t* rows, const int32_t* count, void* stream) {
   if (!rows || !count || !aligned4(rows) || !aligned4(count)) return KVC_E_INVAL;
-  return attention_call(r, q, o, lse, rows, count, stream);
+  return attention_call(r, q, o, lse, nullptr, rows, count, stream);
+}
+
+kvc_status chunk_attn_fwd_rope(kvc_ring* r, const void* q, void* o, float* lse,
+                               const float* rope, const int32_t* rows, const int32_t* count,
+                               void* stream) {
+  if ((rows == nullptr) != (count == nullptr)) return KVC_E_INVAL;
+  if (rows && (!aligned4(rows) || !aligned4(count))) return KVC_E_INVAL;
+  return attention_call(r, q, o, lse, rope, rows, count, stream);
+}
+
+kvc_status kvc_append_chunk(kvc_ring* r, int32_t kind, const void* k, const void* v,
+                            void* stream) {
+  return append(r, kind, k, v, nullptr, stream);
+}
+
+kvc_status kvc_append_chunk_rope(kvc_ring* r, int32_t kind, const void* k, const void* v,
+                                 const float* rope, void* stream) {
+  return append(r, kind, k, v, rope, stream);
 }
 
 kvc_status kvc_edit_mask(const void* z_src, const void* z_edit, int32_t tokens, int32_t channels,

@@ -184,6 +184,35 @@ kvc_status kvc_append_chunk(kvc_ring* ring, int32_t kind, const void* k, const v
 kvc_status chunk_attn_fwd(kvc_ring* ring, const void* q, void* o, float* lse, void* stream);
 
 /*
+ * Rotary position encoding fused into the cache write and the attention's Q
+ * load.  Source: discuss.pytorch.kr "JoyAI-Video-Edit 소개", architecture
+ * section: every block applies M-RoPE to both streams before the masked
+ * self-attention, its angles a fusion of a 3D spatio-temporal RoPE and a 1D
+ * source RoPE (no formula given).  The angles are therefore an input:
+ *   rope  device float32 [rows][d/2][2], 16-byte aligned: (cos, sin) of the
+ *         angle by which features (2i, 2i+1) of each row turn:
+ *           x'_{2i} = x_{2i} cos - x_{2i+1} sin,  x'_{2i+1} = x_{2i} sin + x_{2i+1} cos,
+ *         each product and the sum/difference a float32 operation rounded on
+ *         its own, the result rounded to bf16 (nearest, ties to even), which
+ *         is what the kernels then use.  Only keys and queries turn.
+ *         NULL: no rotation (the plain calls).
+ * kvc_append_chunk_rope: as kvc_append_chunk, with K rotated by rope before
+ *   it is stored (rows as the call's k: m, r or n+s; fp8 rings quantise the
+ *   rotated keys).
+ * chunk_attn_fwd_rope: as chunk_attn_fwd, with q rotated by rope ([n+s] rows)
+ *   as it is loaded; rows / count (both NULL, or both given) select active
+ *   rows as in chunk_attn_fwd_rows.
+ * The result equals the plain calls on K and q rotated beforehand with the
+ * arithmetic above.  Errors as for the plain calls; KVC_E_INVAL for a
+ * misaligned rope or only one of rows / count.
+ */
+kvc_status kvc_append_chunk_rope(kvc_ring* ring, int32_t kind, const void* k, const void* v,
+                                 const float* rope, void* stream);
+kvc_status chunk_attn_fwd_rope(kvc_ring* ring, const void* q, void* o, float* lse,
+                               const float* rope, const int32_t* rows, const int32_t* count,
+                               void* stream);
+
+/*
  * Attention of selected query rows only (LiveEdit's active rows).
  * Source: aitrends.kr, "LiveEdit 실시간 Diffusion 기반 스트리밍 비디오 편집",
  * AR-oriented Mask Cache (methodology and technical-detail sections): only

@@ -254,3 +254,12 @@ def edit_latents(seed: int, chunk: int, grid: tuple[int, int], frames: int, chan
     flat = (frames * rows * cols, channels)
     return (torch.from_numpy(z_src.reshape(flat)).to(torch.bfloat16),
             torch.from_numpy(z_edit.reshape(flat)).to(torch.bfloat16))
+
+
+def rope_table(seed: int, key: int, rows: int, head_dim: int) -> torch.Tensor:
+    """A float32 rotation table [rows, head_dim/2, 2] of (cos, sin) for
+    uniformly drawn angles in [-pi, pi): a stand-in for the model's fused
+    3D/1D position angles, whose formula the pages do not give."""
+    ss = np.random.SeedSequence([seed, key, rows, head_dim, 99])
+    ang = np.random.default_rng(ss).uniform(-math.pi, math.pi, (rows, head_dim // 2))
+    return torch.from_numpy(np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32))

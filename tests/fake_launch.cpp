@@ -35,6 +35,7 @@ struct Record {
   uint64_t stream;
   uint64_t qrows;     // attention: active-row map (0: all rows)
   uint64_t qcount;    // attention: active-row count
+  uint64_t rope;      // write: K rotation table; attention: q rotation table
 };
 
 std::vector<Record> g_log;
@@ -64,6 +65,7 @@ kvc_status launch_cache_write(const CacheWriteDesc& d, void* stream) {
   r.kv_dtype = d.kv_dtype;
   r.k_scale = reinterpret_cast<uint64_t>(d.k_scale);
   r.stream = reinterpret_cast<uint64_t>(stream);
+  r.rope = reinterpret_cast<uint64_t>(d.rope);
   g_log.push_back(r);
   return KVC_OK;
 }
@@ -87,6 +89,7 @@ kvc_status launch_attention(const AttnDesc& d, void* stream) {
   r.stream = reinterpret_cast<uint64_t>(stream);
   r.qrows = reinterpret_cast<uint64_t>(d.qrows);
   r.qcount = reinterpret_cast<uint64_t>(d.qcount);
+  r.rope = reinterpret_cast<uint64_t>(d.qrope);
   g_log.push_back(r);
   return KVC_OK;
 }

@@ -28,7 +28,8 @@ class Record(ctypes.Structure):
                 ("seg_pitch", ctypes.c_int32 * kv.KVC_MAX_SEGMENTS),
                 ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("k_scale", ctypes.c_uint64), ("stream", ctypes.c_uint64),
-                ("qrows", ctypes.c_uint64), ("qcount", ctypes.c_uint64)]
+                ("qrows", ctypes.c_uint64), ("qcount", ctypes.c_uint64),
+                ("rope", ctypes.c_uint64)]
 
 
 @pytest.fixture(scope="module")
@@ -443,3 +444,69 @@ def test_token_groups(lib, W, m, rr, s):
         if st == kv.KVC_OK:
             assert view.rows == n
     r.close()
+
+
+def test_rope_tables_follow_the_rows(lib):
+    # the K rotation table of a STAGE/COMMIT covers n + s rows: the source
+    # write gets the table from row n on (n * d floats further); the
+    # attention record carries q's table; misaligned tables and a rows map
+    # without a count are rejected
+    H, d, n, s = 2, 128, 100, 30
+    r = FakeRing(lib, H=H, d=d, n=n, m=8, W=1, s=s)
+    P = ctypes.c_void_p
+    tab = 0x900000
+    assert lib.kvc_append_chunk_rope(r.h, kv.KVC_COND, P(0x1000), P(0x2000), P(tab), P(0)) == 0
+    assert r.last().rope == tab
+    before = r.count()
+    assert lib.kvc_append_chunk_rope(r.h, kv.KVC_STAGE, P(0x1000), P(0x2000), P(tab), P(0)) == 0
+    assert r.count() - before == 2
+    w0 = Record()
+    lib.kvcfake_get(before, ctypes.byref(w0))
+    assert w0.rope == tab and w0.rows == n
+    assert r.last().rope == tab + n * d * 4 and r.last().rows == s
+    assert lib.kvc_append_chunk_rope(r.h, kv.KVC_STAGE, P(0x1000), P(0x2000), P(tab + 4),
+                                     P(0)) == kv.KVC_E_INVAL
+    assert lib.kvc_append_chunk(r.h, kv.KVC_STAGE, P(0x1000), P(0x2000), P(0)) == 0
+    assert r.last().rope == 0
+    assert lib.chunk_attn_fwd_rope(r.h, P(0x3000), P(0x4000), None, P(tab), None, None,
+                                   P(0)) == 0
+    a = r.last()
+    assert a.kind == 1 and a.rope == tab and a.qrows == 0 and a.rows == n + s
+    assert lib.chunk_attn_fwd_rope(r.h, P(0x3000), P(0x4000), None, P(tab), P(0x5000), None,
+                                   P(0)) == kv.KVC_E_INVAL
+    assert lib.chunk_attn_fwd_rope(r.h, P(0x3000), P(0x4000), None, P(tab + 8), None, None,
+                                   P(0)) == kv.KVC_E_INVAL
+    assert lib.chunk_attn_fwd_rope(r.h, P(0x3000), P(0x4000), None, None, P(0x5000), P(0x6000),
+                                   P(0)) == 0
+    a = r.last()
+    assert (a.rope, a.qrows, a.qcount) == (0, 0x5000, 0x6000)
+    r.close()
+
+
+def test_edit_mask_arguments(lib):
+    P = ctypes.c_void_p
+    ok = (P(0x1000), P(0x2000), 100, 16, ctypes.c_float(1.0), -1, P(0x3000), P(0x4000), P(0))
+    lib.kvcfake_reset()
+    assert lib.kvc_edit_mask(*ok) == 0
+    r = Record()
+    lib.kvcfake_get(0, ctypes.byref(r))
+    assert (r.kind, r.rows, r.pitch, r.nseg, r.dst_k, r.dst_vt) == (2, 100, 16, -1, 0x3000, 0x4000)
+    bad = [
+        (P(0), P(0x2000), 100, 16, ctypes.c_float(1.0), -1, P(0x3000), P(0x4000), P(0)),
+        (P(0x1000), P(0x2000), 0, 16, ctypes.c_float(1.0), -1, P(0x3000), P(0x4000), P(0)),
+        (P(0x1000), P(0x2000), kv.KVC_MAX_MASK_TOKENS + 1, 16, ctypes.c_float(1.0), 3,
+         P(0x3000), P(0x4000), P(0)),
+        (P(0x1000), P(0x2000), 100, kv.KVC_MAX_MASK_CHANNELS + 1, ctypes.c_float(1.0), 3,
+         P(0x3000), P(0x4000), P(0)),
+        (P(0x1000), P(0x2000), 100, 16, ctypes.c_float(-1.0), -1, P(0x3000), P(0x4000), P(0)),
+        (P(0x1000), P(0x2000), 100, 16, ctypes.c_float(float("nan")), -1, P(0x3000),
+         P(0x4000), P(0)),
+        (P(0x1000), P(0x2000), 100, 16, ctypes.c_float(1.0), -1, P(0x3002), P(0x4000), P(0)),
+        (P(0x1001), P(0x2000), 100, 16, ctypes.c_float(1.0), -1, P(0x3000), P(0x4000), P(0)),
+    ]
+    for b in bad:
+        assert lib.kvc_edit_mask(*b) == kv.KVC_E_INVAL
+    # a negative tau is fine in top-k mode (ignored)
+    assert lib.kvc_edit_mask(P(0x1000), P(0x2000), 100, 16, ctypes.c_float(-1.0), 5, P(0x3000),
+                             P(0x4000), P(0)) == 0
+    assert lib.kvcfake_count() == 2
