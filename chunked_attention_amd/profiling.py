@@ -37,7 +37,8 @@ def _one(dirname: str, pattern: str) -> str:
 
 
 def short_name(name: str) -> str:
-    for key in (ATTN, ATTN8, "cache_write", "cache_amax", "cache_quant", "fill_u32", CALIB):
+    for key in (ATTN, ATTN8, "cache_write", "cache_amax", "cache_quant", "edit_mask_kernel",
+                "fill_u32", CALIB):
         if key in name:
             if key in (ATTN, ATTN8):
                 i = name.find(key + "<")
