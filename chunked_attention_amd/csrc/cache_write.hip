@@ -22,7 +22,6 @@
 // HBM-bound: each element is read once and written once.  One workgroup
 // handles 64 rows of one head; V goes through LDS for the transpose.
 #include "device_common.hpp"
-#include "e4m3.hpp"
 #include "kvc_internal.hpp"
 
 namespace kvc {
@@ -94,6 +93,19 @@ __global__ __launch_bounds__(kThreads) void cache_write_bf16(
 }
 
 // ----------------------------------------------------------------- fp8 ----
+
+// E4M3 codes of two float32 values (byte 0: a, byte 1: b): nearest, ties to
+// even, saturating at +-448, NaN -> 0x7F with the sign kept (the rule
+// written out in e4m3.hpp), taken by the hardware conversion (nearest-even on
+// finite values up to 448) after an explicit saturation.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
+  const float ca = fminf(fmaxf(a, -448.0f), 448.0f);
+  const float cb = fminf(fmaxf(b, -448.0f), 448.0f);
+  uint32_t r = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false)) & 0xFFFFu;
+  if (a != a) r = (r & 0xFF00u) | ((__float_as_uint(a) >> 24) & 0x80u) | 0x7Fu;
+  if (b != b) r = (r & 0x00FFu) | (((__float_as_uint(b) >> 24) & 0x80u) | 0x7Fu) << 8;
+  return r;
+}
 // Pass 1: per (head, 64-row block) largest magnitude of K and of V.
 
 template <int D>
@@ -201,12 +213,12 @@ __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
       const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t k0 = e4m3_from_float(__fdiv_rn(bf16_bits_to_float(kw[j] & 0xFFFFu), sk));
-        const uint32_t k1 = e4m3_from_float(__fdiv_rn(bf16_bits_to_float(kw[j] >> 16), sk));
-        const uint32_t v0 = e4m3_from_float(__fdiv_rn(bf16_bits_to_float(vw[j] & 0xFFFFu), sv));
-        const uint32_t v1 = e4m3_from_float(__fdiv_rn(bf16_bits_to_float(vw[j] >> 16), sv));
-        kc[j >> 1] |= (k0 | (k1 << 8)) << (16 * (j & 1));
-        vc[j >> 1] |= (v0 | (v1 << 8)) << (16 * (j & 1));
+        const uint32_t k01 = e4m3x2(__fdiv_rn(bf16_bits_to_float(kw[j] & 0xFFFFu), sk),
+                                    __fdiv_rn(bf16_bits_to_float(kw[j] >> 16), sk));
+        const uint32_t v01 = e4m3x2(__fdiv_rn(bf16_bits_to_float(vw[j] & 0xFFFFu), sv),
+                                    __fdiv_rn(bf16_bits_to_float(vw[j] >> 16), sv));
+        kc[j >> 1] |= k01 << (16 * (j & 1));
+        vc[j >> 1] |= v01 << (16 * (j & 1));
       }
     }
     *reinterpret_cast<uint2*>(kd + (static_cast<size_t>(h) * pitch + r) * D + ch * 8) =

@@ -1,5 +1,7 @@
-// OCP FP8 E4M3 ("fn") encoder used by the fp8 cache write.  Built for the
-// device and, for CPU tests, for the host.
+// OCP FP8 E4M3 ("fn") encoder: the encoding rule of the fp8 cache write,
+// written out in software.  The device takes the same rule with the hardware
+// conversion (cache_write.hip, e4m3x2); this version serves the CPU tests of
+// the rule against the oracle.
 #pragma once
 
 #include <cmath>

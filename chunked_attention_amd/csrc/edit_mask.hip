@@ -14,13 +14,16 @@
 // tokens; the work is microseconds next to the attention it feeds):
 //   1. squared distance of every token into LDS (float64, channels summed in
 //      order, every operation rounded on its own, so a plain CPU loop gets
-//      the same bits);
+//      the same bits; four tokens per thread loaded at once);
 //   2. threshold mode: flag distances above tau^2.  Top-k mode: radix-select
 //      the keep-th largest distance over its 64-bit order-preserving key
-//      (eight 8-bit digit passes with an LDS histogram), flag every larger
-//      key and, among keys equal to it, the lowest indices up to keep;
+//      (eight 8-bit digit passes; one LDS histogram per wave, so colliding
+//      atomics stay within a wave, summed before one wave finds the bin),
+//      flag every larger key and, among keys equal to it, the lowest indices
+//      up to keep;
 //   3. compact: thread t owns tokens 16t .. 16t+15; a prefix sum of the flag
-//      counts gives each thread its output position.
+//      counts (lane shuffles, then the waves' totals) gives each thread its
+//      output position.
 #include "device_common.hpp"
 #include "kvc_internal.hpp"
 
@@ -41,29 +44,53 @@ __device__ __forceinline__ double add_sq(double acc, uint32_t e, uint32_t s) {
   return acc + sq;
 }
 
-// sum_c (e_c - s_c)^2 for one token, float64, channels in order; NaN -> -1
-// (a NaN distance is never above the threshold and ranks last).  `vec`:
-// rows are whole 16-byte chunks (8 channels), read 16 bytes at a time.
-__device__ double distance_sq(const uint16_t* __restrict__ zs, const uint16_t* __restrict__ ze,
-                              int channels, int token, bool vec) {
-  const uint16_t* s = zs + static_cast<size_t>(token) * channels;
-  const uint16_t* e = ze + static_cast<size_t>(token) * channels;
-  double acc = 0.0;
+__device__ __forceinline__ double nan_last(double acc) { return acc != acc ? -1.0 : acc; }
+
+// sum_c (e_c - s_c)^2 of the tokens i0 + u * kThreads (u < kTok) into dist[],
+// float64, channels in order for each token; NaN -> -1 (a NaN distance is
+// never above the threshold and ranks last).  `vec`: rows are whole
+// 16-byte chunks (8 channels), read 16 bytes at a time, the chunks of all
+// kTok tokens loaded before any is used so their latencies overlap.
+template <int kTok>
+__device__ void distances(const uint16_t* __restrict__ zs, const uint16_t* __restrict__ ze,
+                          int tokens, int channels, int i0, bool vec, double* __restrict__ dist) {
+  double acc[kTok];
+#pragma unroll
+  for (int u = 0; u < kTok; ++u) acc[u] = 0.0;
   if (vec) {
     for (int c = 0; c < channels; c += 8) {
-      const uint4 ev = ld16(e + c), sv = ld16(s + c);
-      const uint32_t ew[4] = {ev.x, ev.y, ev.z, ev.w};
-      const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+      uint4 ev[kTok], sv[kTok];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc = add_sq(acc, ew[q] & 0xFFFFu, sw[q] & 0xFFFFu);
-        acc = add_sq(acc, ew[q] >> 16, sw[q] >> 16);
+      for (int u = 0; u < kTok; ++u) {
+        const int i = min(i0 + u * kThreads, tokens - 1);   // in bounds; unused if past the end
+        ev[u] = ld16(ze + static_cast<size_t>(i) * channels + c);
+        sv[u] = ld16(zs + static_cast<size_t>(i) * channels + c);
+      }
+#pragma unroll
+      for (int u = 0; u < kTok; ++u) {
+        const uint32_t ew[4] = {ev[u].x, ev[u].y, ev[u].z, ev[u].w};
+        const uint32_t sw[4] = {sv[u].x, sv[u].y, sv[u].z, sv[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[u] = add_sq(acc[u], ew[q] & 0xFFFFu, sw[q] & 0xFFFFu);
+          acc[u] = add_sq(acc[u], ew[q] >> 16, sw[q] >> 16);
+        }
       }
     }
   } else {
-    for (int c = 0; c < channels; ++c) acc = add_sq(acc, e[c], s[c]);
+#pragma unroll
+    for (int u = 0; u < kTok; ++u) {
+      const int i = min(i0 + u * kThreads, tokens - 1);
+      const uint16_t* s = zs + static_cast<size_t>(i) * channels;
+      const uint16_t* e = ze + static_cast<size_t>(i) * channels;
+      for (int c = 0; c < channels; ++c) acc[u] = add_sq(acc[u], e[c], s[c]);
+    }
   }
-  return acc != acc ? -1.0 : acc;
+#pragma unroll
+  for (int u = 0; u < kTok; ++u) {
+    const int i = i0 + u * kThreads;
+    if (i < tokens) dist[i] = nan_last(acc[u]);
+  }
 }
 
 // unsigned key with the order of the float64 value
@@ -72,22 +99,32 @@ __device__ __forceinline__ unsigned long long order_key(double d) {
   return (u >> 63) ? ~u : (u | (1ULL << 63));
 }
 
-// exclusive prefix sum of v over the workgroup (Hillis-Steele in LDS); also
-// returns the total
-__device__ int exclusive_scan(int v, int (&buf)[kThreads], int& total) {
+constexpr int kWaves = kThreads / 64;
+
+// exclusive prefix sum of v over the workgroup, and its total: an inclusive
+// scan inside each wave (lane shuffles), then the waves' totals through LDS
+__device__ int exclusive_scan(int v, int (&wave_sum)[kWaves], int& total) {
   const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int add = tid >= off ? buf[tid - off] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
   }
-  total = buf[kThreads - 1];
-  const int incl = buf[tid];
+  if (lane == 63) wave_sum[wave] = x;
   __syncthreads();
-  return incl - v;
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int ws = wave_sum[w];
+    before += w < wave ? ws : 0;
+    total += ws;
+  }
+  __syncthreads();   // wave_sum may be reused by the next scan
+  return before + x - v;
 }
 
 template <bool kTopK>
@@ -95,12 +132,14 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
     const uint16_t* __restrict__ zs, const uint16_t* __restrict__ ze, int tokens, int channels,
     double tau2, int keep, bool vec, int* __restrict__ rows, int* __restrict__ count) {
   __shared__ double dist[KVC_MAX_MASK_TOKENS];
-  __shared__ int scan[kThreads];
+  __shared__ int scan[kWaves];
+  __shared__ unsigned whist[kWaves][256];   // per-wave histograms (less atomic contention)
   __shared__ unsigned hist[256];
   __shared__ unsigned long long s_prefix;
   __shared__ int s_need;
   const int tid = threadIdx.x;
-  for (int i = tid; i < tokens; i += kThreads) dist[i] = distance_sq(zs, ze, channels, i, vec);
+  for (int i0 = tid; i0 < tokens; i0 += 4 * kThreads)
+    distances<4>(zs, ze, tokens, channels, i0, vec, dist);
   __syncthreads();
 
   const int lo = tid * kPerThread;
@@ -111,17 +150,31 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
   } else {
     const int k = min(keep, tokens);
     if (k > 0) {
+      // this thread's keys, in registers for all passes (tokens past the end
+      // get key 0, below every real key, and are never counted)
+      unsigned long long key[kPerThread];
+#pragma unroll
+      for (int j = 0; j < kPerThread; ++j)
+        key[j] = lo + j < tokens ? order_key(dist[lo + j]) : 0ULL;
       // the k-th largest key: fix 8 bits per pass from the top, keeping
       // `need` = how many of the keys matching the prefix are still wanted
       unsigned long long prefix = 0, pmask = 0;
       int need = k;
+      const int wv = tid >> 6;
       for (int p = 56; p >= 0; p -= 8) {
-        if (tid < 256) hist[tid] = 0;
+        for (int b = tid; b < kWaves * 256; b += kThreads) (&whist[0][0])[b] = 0;
         __syncthreads();
+#pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
-          if (lo + j >= tokens) break;
-          const unsigned long long u = order_key(dist[lo + j]);
-          if ((u & pmask) == prefix) atomicAdd(&hist[(u >> p) & 255], 1u);
+          const unsigned long long u = key[j];
+          if (lo + j < tokens && (u & pmask) == prefix) atomicAdd(&whist[wv][(u >> p) & 255], 1u);
+        }
+        __syncthreads();
+        if (tid < 256) {
+          unsigned sum = 0;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) sum += whist[w][tid];
+          hist[tid] = sum;
         }
         __syncthreads();
         if (tid < 64) {
@@ -158,11 +211,13 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
       // larger keys are in; of the keys equal to the k-th, the first `need`
       // by index
       unsigned eq = 0;
+#pragma unroll
       for (int j = 0; j < kPerThread; ++j) {
-        if (lo + j >= tokens) break;
-        const unsigned long long u = order_key(dist[lo + j]);
-        if (u > prefix) flags |= 1u << j;
-        else if (u == prefix) eq |= 1u << j;
+        const unsigned long long u = key[j];
+        if (lo + j < tokens) {
+          if (u > prefix) flags |= 1u << j;
+          else if (u == prefix) eq |= 1u << j;
+        }
       }
       int unused;
       int before = exclusive_scan(__popc(eq), scan, unused);

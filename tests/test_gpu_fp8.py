@@ -221,3 +221,35 @@ def test_fp8_repeat_runs_are_bitwise_deterministic():
         kc, vc = s.kv_clean(t)
         r.commit(kc.cuda(), vc.cuda())
         r.evict()
+
+
+def test_fp8_codes_of_crafted_values():
+    # amax = 448 per head makes the scale exactly 1, so the stored codes are
+    # the E4M3 codes of the values themselves: every code, every midpoint
+    # between neighbours (ties to even) and one bf16 step either side of it,
+    # the subnormal range, zeros of both signs and NaN, against O3
+    pos = O3.decode_table()[:127].astype(np.float64)          # 0 .. 448
+    mids = (pos[1:] + pos[:-1]) / 2
+    vals = [pos, -pos, mids, -mids]
+    b = torch.from_numpy(mids.astype(np.float32)).to(torch.bfloat16)
+    up = torch.nextafter(b, torch.full_like(b, 1e4)).float().numpy()
+    dn = torch.nextafter(b, torch.full_like(b, -1e4)).float().numpy()
+    vals += [up, dn, -up, -dn, np.array([0.0, -0.0, 2.0 ** -10, 3 * 2.0 ** -10, -(2.0 ** -12)])]
+    x = np.concatenate(vals)
+    d = 128
+    rows = (x.size + d - 1) // d + 1
+    flat = np.zeros(rows * d, dtype=np.float32)
+    flat[:x.size] = x
+    flat[-1] = 448.0                     # amax of the head: scale 1
+    flat[-2] = np.nan
+    k = torch.from_numpy(flat.reshape(rows, 1, d)).to(torch.bfloat16)
+    assert torch.equal(k.float().reshape(-1)[:x.size], torch.from_numpy(x.astype(np.float32))), \
+        "crafted values must be bf16-representable"
+    r = kv.Ring(1, d, 64, rows, 0, kv_dtype="fp8_e4m3")
+    r.cond(k.cuda(), k.cuda())
+    torch.cuda.synchronize()
+    K, _, ks, _, n = r.slot_tensors(-1)
+    assert n == rows and float(ks.cpu()[0]) == 1.0
+    got = K.cpu().numpy()[0, :rows].reshape(-1)
+    want = O3.encode(k.float().numpy().reshape(-1))
+    assert np.array_equal(got, want)
