@@ -186,13 +186,19 @@ void attn_fwd_bf16(const AttnArgs a) {
 
   const Split sp = make_split(a);
   if (w >= sp.nwg) return;
-  for (long long x = range_begin(w, sp), xe = range_begin(w + 1, sp); x < xe;) {
-    const int r = static_cast<int>(x / a.ntiles);
-    const int t0 = static_cast<int>(x % a.ntiles);
-    const long long rest = xe - x;
-    const int t1 = rest < a.ntiles - t0 ? t0 + static_cast<int>(rest) : a.ntiles;
-    const bool first_piece = x == range_begin(w, sp);
-    x += t1 - t0;
+  // The pieces of this workgroup's range (one per row it touches) run last
+  // first: every workgroup then starts at the first step of a row, and the
+  // workgroups sharing a head walk its keys nearly in step, so one copy of
+  // each tile in L2 serves them all.
+  const long long xb = range_begin(w, sp);
+  for (long long e = range_begin(w + 1, sp); e > xb;) {
+    const int r = static_cast<int>((e - 1) / a.ntiles);
+    const long long row_start = static_cast<long long>(r) * a.ntiles;
+    const long long s0 = xb > row_start ? xb : row_start;
+    const int t0 = static_cast<int>(s0 - row_start);
+    const int t1 = static_cast<int>(e - row_start);
+    const bool first_piece = s0 == xb;
+    e = s0;
     const int h = r / sp.nqt;
     const int qbase = (r - h * sp.nqt) * kBq + wave * kQW;
 
