@@ -395,20 +395,19 @@ def gpu_telemetry():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_720p_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "chunked_attention_amd", "csrc", "attn_fwd.hip")
 
 
 def measured_traffic():
     """HBM bytes per launch of the attention kernel from the committed
-    counter summary, or None if there is none or the kernel source changed
+    counter summary, or None if there is none or the kernel's code changed
     since the counters were taken."""
-    import hashlib
+    from chunked_attention_amd.profiling import kernel_code_digest
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        sha = kernel_code_digest()
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_code_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
 

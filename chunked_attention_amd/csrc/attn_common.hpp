@@ -4,12 +4,14 @@
 // the end of a row piece (normalise and store, or hand a partial result to
 // the piece that merges the row).
 //
-// Work: a "row" is 128 queries of one head; its keys are T tiles of 64 keys
-// over all visible segments.  A workgroup of 4 waves (32 queries each) runs
-// one row piece at a time; nwg persistent workgroups split the R*T (row,
-// tile) steps into equal contiguous ranges.  A row cut between workgroups is
-// finished by the last piece to arrive, which merges every piece's partial
-// (O, reference, sums) in piece order, so results do not depend on timing.
+// Work: a "row" is 128 queries of one head; its keys are T steps (a kernel-
+// defined number of keys: 32 for bf16, 64 for fp8) over all visible
+// segments.  A workgroup of 4 waves (32 queries each) runs one row piece at a
+// time; nwg persistent workgroups split the R*T (row, step) pairs into equal
+// contiguous ranges.  A row cut between workgroups is finished by the last
+// piece to arrive, which merges every piece's partial (O, reference, sums) in
+// piece order, so results do not depend on timing.  Active-row calls take
+// the split at run time from a device-side query count (make_split).
 #pragma once
 
 #include <algorithm>

@@ -1,11 +1,12 @@
 // K2: chunk-causal sink+window attention forward, bf16 MFMA, gfx950.
 //
-// For every query of the current chunk and every head, softmax attention over
-// the visible keys: condition tokens, the sink chunk, the window chunks and
-// the current chunk (discuss.pytorch.kr "JoyAI-Video-Edit 소개", chunk-wise
+// For every query of the current chunk (and of its source tokens) and every
+// head, softmax attention over the visible keys: condition and reference
+// tokens, the sink chunk, the window chunks, the current chunk and its source
+// tokens (discuss.pytorch.kr "JoyAI-Video-Edit 소개", chunk-wise
 // autoregressive adaptation section: bidirectional within the chunk, causal
-// across chunks through a sliding window plus the first chunk as global
-// sink).  The visible set is never concatenated: the kernel walks the ring's
+// across chunks through a sliding window plus the first chunk as global sink;
+// architecture section: the token groups and the mask between them).  The visible set is never concatenated: the kernel walks the ring's
 // segment table (cache slots in logical order) tile by tile.
 //
 // Work: a "row" is 128 queries of one head; its keys are T steps of 32 keys

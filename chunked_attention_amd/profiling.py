@@ -23,7 +23,23 @@ import os
 import statistics
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-KERNEL_SOURCE = os.path.join(ROOT, "chunked_attention_amd", "csrc", "attn_fwd.hip")
+# the sources the bf16 attention kernel is compiled from
+KERNEL_SOURCES = [os.path.join(ROOT, "chunked_attention_amd", "csrc", f)
+                  for f in ("attn_fwd.hip", "attn_common.hpp", "device_common.hpp",
+                            "kvc_internal.hpp")] + [os.path.join(ROOT, "include", "kvc.h")]
+
+
+def kernel_code_digest() -> str:
+    """sha256 of the attention kernel's sources with comments and whitespace
+    removed: it changes when the code changes, not when a comment does."""
+    import re
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        txt = open(path, encoding="utf-8").read()
+        txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", " ", txt)
+        h.update(" ".join(txt.split()).encode())
+    return h.hexdigest()
 ATTN = "attn_fwd_bf16"
 ATTN8 = "attn_fwd_fp8"
 CALIB = "neg_kernel"
@@ -134,8 +150,8 @@ def main(argv=None):
         open(args.out, "w").write(stats_md(args.dir, args.cmd, args.steady))
         return 0
     res, total = traffic(args.fetch, args.write, args.calib_mib, args.steady)
-    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-    rec = {"kernel": ATTN, "workload": args.workload, "kernel_source_sha256": sha,
+    sha = kernel_code_digest()
+    rec = {"kernel": ATTN, "workload": args.workload, "kernel_code_sha256": sha,
            "hbm_bytes_per_launch": round(total), "counters": res,
            "commands": {"FETCH_SIZE": args.cmd_fetch, "WRITE_SIZE": args.cmd_write}}
     json.dump(rec, open(args.out, "w"), indent=1)
@@ -153,7 +169,7 @@ def main(argv=None):
           f"{f['scale']:.4f} | {f['attn_bytes'] / 1e6:.1f} MB |",
           f"| WRITE_SIZE | {wr['attn_kib_per_dispatch']:.0f} | {wr['calib_kib_per_dispatch']:.0f} | "
           f"{wr['scale']:.4f} | {wr['attn_bytes'] / 1e6:.1f} MB |",
-          "", f"Total HBM bytes per launch: {total / 1e6:.1f} MB.  Kernel source sha256 "
+          "", f"Total HBM bytes per launch: {total / 1e6:.1f} MB.  Kernel code sha256 "
           f"{sha[:16]}...", ""]
     open(args.md, "w").write("\n".join(md))
     print(json.dumps({"hbm_bytes_per_launch": round(total)}))
