@@ -284,6 +284,13 @@ void attn_fwd_bf16(const AttnArgs a) {
       auto step = [&](auto u_tag) {
         constexpr int U = decltype(u_tag)::value;
         constexpr int CUR = U & 1;
+        // Two workgroups share each CU, one wave of each per SIMD.  The
+        // issue arbiter favours the older wave, so with equal priorities one
+        // workgroup runs well ahead and the other finishes its (equal) range
+        // alone at one wave per SIMD.  Raising the priority on every other
+        // step lets the two waves take turns being favoured, and the pair
+        // ends together.
+        __builtin_amdgcn_s_setprio(U & 1);
         dma_k(std::integral_constant<int, U>{}, ck);
         dma_v(std::integral_constant<int, (U + 3) & 3>{}, cv);
         bf16x8_t kops[kDS];

@@ -363,6 +363,9 @@ void attn_fwd_fp8(const AttnArgs a) {
       };
       auto tile = [&](auto u_tag) {
         constexpr int U = decltype(u_tag)::value;
+        // take turns with the other workgroup's wave on this SIMD (the
+        // arbiter favours the older wave; see the bf16 kernel)
+        __builtin_amdgcn_s_setprio(U & 1);
         dma_k(std::integral_constant<int, (U + 3) & 3>{}, ck);
         dma_v(std::integral_constant<int, (U + 2) & 3>{}, cv);
         half_tile(u_tag, std::integral_constant<int, 0>{});
