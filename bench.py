@@ -203,22 +203,30 @@ def run_stream_bench(w, args, device, flat: bool):
     attn_events, write_events, step_events, mask_events = [], [], [], []
     kv_len = [0]        # keys attended by the timed calls (largest)
 
+    # Timed chunks record exactly one event between consecutive launches (an
+    # event record itself takes a few microseconds on the stream): `last` is
+    # the event that closes the previous launch and opens the next, carried
+    # from one timed chunk to the next (the first one starts at `start`).
+    carry = {"last": None}
+
     def chunk(t: int, timed: bool):
         c = t % pool
+        last = None
         if timed:
-            e = next(ev_iter)
-            e.record(stream)
-            step_events.append(e)
+            last = carry["last"]
+            if last is None:
+                last = next(ev_iter)
+                last.record(stream)
+            step_events.append(last)
         if keep is not None:
             # LiveEdit: this chunk's active rows from the previous chunk's
             # latents, on the device (shared by every layer and step)
-            if timed:
-                m0, m1 = next(ev_iter), next(ev_iter)
-                m0.record(stream)
             kv.kvc_edit_mask(*inp.latents[c], keep=keep, rows=rows_buf, count=count_buf)
             if timed:
+                m1 = next(ev_iter)
                 m1.record(stream)
-                mask_events.append((m0, m1))
+                mask_events.append((last, m1))
+                last = m1
 
         def attend(r, q, out):
             if keep is None:
@@ -229,8 +237,7 @@ def run_stream_bench(w, args, device, flat: bool):
         for st in range(w.steps):
             for li, r in enumerate(rings):
                 if timed:
-                    e0, e1, e2 = next(ev_iter), next(ev_iter), next(ev_iter)
-                    e0.record(stream)
+                    e0, e1, e2 = last, next(ev_iter), next(ev_iter)
                     r.stage(*inp.noisy[c][st], rope=inp.rope_k[c])
                     e1.record(stream)
                     attend(r, inp.q[c][st], outs[li & 1])
@@ -239,16 +246,17 @@ def run_stream_bench(w, args, device, flat: bool):
                         kv_len[0] = max(kv_len[0], r.info().kv_len)
                     write_events.append((e0, e1))
                     attn_events.append((e1, e2))
+                    last = e2
                 else:
                     r.stage(*inp.noisy[c][st], rope=inp.rope_k[c])
                     attend(r, inp.q[c][st], outs[li & 1])
         for li, r in enumerate(rings):
             if timed:
-                e0, e1 = next(ev_iter), next(ev_iter)
-                e0.record(stream)
+                e0, e1 = last, next(ev_iter)
                 r.commit(*inp.clean[c], rope=inp.rope_k[c])
                 e1.record(stream)
                 write_events.append((e0, e1))
+                last = e1
                 if args.clean_pass:
                     # the clean pass: one more attention call per layer over
                     # the committed chunk (queries of the clean latent; the
@@ -257,11 +265,13 @@ def run_stream_bench(w, args, device, flat: bool):
                     attend(r, inp.q[c][0], outs[li & 1])
                     e2.record(stream)
                     attn_events.append((e1, e2))
+                    last = e2
             else:
                 r.commit(*inp.clean[c], rope=inp.rope_k[c])
                 if args.clean_pass:
                     attend(r, inp.q[c][0], outs[li & 1])
             r.evict()
+        carry["last"] = last
 
     def clock_warmup(t: int) -> int:
         # The GPU raises its shader clock over tens of milliseconds of
@@ -308,10 +318,13 @@ def run_stream_bench(w, args, device, flat: bool):
         torch.cuda.synchronize()
         t_first = t
         start.record(stream)
+        carry["last"] = start
+        h0 = time.perf_counter()
         for _ in range(steps):
             chunk(t, True)
             t += 1
         end.record(stream)
+        host_s = time.perf_counter() - h0   # enqueue time (the GPU runs behind)
         torch.cuda.synchronize()
     finally:
         gc.enable()
@@ -320,6 +333,7 @@ def run_stream_bench(w, args, device, flat: bool):
     step_ms = [step_events[i].elapsed_time(step_events[i + 1])
                for i in range(len(step_events) - 1)] + [step_events[-1].elapsed_time(end)]
     res = {
+        "host_ms_per_step": host_s * 1e3 / steps,
         "ms_per_step": total_ms / steps,
         "steps": steps,
         "warmup": warmup,
@@ -532,6 +546,8 @@ def main() -> int:
                                 if r["mask_ms"] else None),
         "step_ms_median": round(med, 4),
         "step_ms_max_dev_pct": dev(steps_ms, med),
+        "step_ms_p99": round(sorted(steps_ms)[min(len(steps_ms) - 1, int(0.99 * len(steps_ms)))], 4),
+        "host_enqueue_ms_per_step": round(r["host_ms_per_step"], 4),
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
