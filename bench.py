@@ -455,7 +455,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the attention "
-              "path would shard by heads with no exchange inside attention, but this build "
+              "path would shard by heads with no exchange inside attention, but this benchmark "
               "runs and reports a single MI355X.", file=sys.stderr)
         return 2
 
@@ -501,7 +501,10 @@ def main() -> int:
     steps_ms = r["step_ms"]
     med = statistics.median(steps_ms)
     dev = lambda xs, m: round(100 * max(abs(x - m) for x in xs) / m, 2)
-    traffic = measured_traffic() if (w.name == "720p" and not fp8) else None
+    # the committed counter record is for the plain 720p call (full rows, no
+    # rotation); any other launch gets no traffic figure
+    plain_720p = w.name == "720p" and not fp8 and queries is None and not args.rope
+    traffic = measured_traffic() if plain_720p else None
     out = {
         "metric": "chunk-attn TFLOP/s + chunks/s at 720p chunk shape; % of MFMA peak",
         "value": round(value, 2),

@@ -423,7 +423,7 @@ const char* kvc_status_str(kvc_status s) {
     case KVC_E_STATE: return "KVC_E_STATE: call not allowed in the ring's current state";
     case KVC_E_NOMEM: return "KVC_E_NOMEM: buffer smaller than kvc_required_bytes";
     case KVC_E_DEVICE: return "KVC_E_DEVICE: HIP runtime error";
-    case KVC_E_UNSUPPORTED: return "KVC_E_UNSUPPORTED: not supported by this build";
+    case KVC_E_UNSUPPORTED: return "KVC_E_UNSUPPORTED: not supported by this library";
     default: return "unknown kvc status";
   }
 }

@@ -59,7 +59,7 @@ typedef int32_t kvc_status;
 #define KVC_E_STATE       (-2)  /* call not allowed in the ring's current state */
 #define KVC_E_NOMEM       (-3)  /* caller buffer smaller than kvc_required_bytes */
 #define KVC_E_DEVICE      (-4)  /* the HIP runtime reported an error */
-#define KVC_E_UNSUPPORTED (-5)  /* valid request this build does not implement */
+#define KVC_E_UNSUPPORTED (-5)  /* valid request this library does not implement */
 
 /* K/V storage type of a ring */
 #define KVC_KV_BF16      0   /* bf16, bit copies of the caller's K/V */
