@@ -394,8 +394,9 @@ class Ring:
         return kvc_get_segments(self.handle)
 
     def slot_tensors(self, which: int):
-        """Views of a stored slot: K [H][pitch][d], Vt [H][d][pitch] (bf16 or
-        uint8 codes) and, for fp8 rings, the float32 scales [H] of K and V."""
+        """Views of a stored slot: K [H][pitch][d], Vt [H][pitch/T][d][T]
+        (tiles of T = 32 keys for bf16, 64 for fp8; bf16 values or uint8
+        codes) and, for fp8 rings, the float32 scales [H] of K and V."""
         import torch
         v = kvc_get_slot(self.handle, which)
         base = self.buf.data_ptr()
@@ -406,7 +407,8 @@ class Ring:
             return self.buf[ptr - base: ptr - base + nbytes]
         dt = torch.bfloat16 if v.elem_bytes == 2 else torch.uint8
         k = part(v.k, n).view(dt).view(H, v.pitch, d)
-        vt = part(v.vt, n).view(dt).view(H, d, v.pitch)
+        T = 32 if v.elem_bytes == 2 else 64
+        vt = part(v.vt, n).view(dt).view(H, v.pitch // T, d, T)
         if v.k_scale:
             ks = part(v.k_scale, 4 * H).view(torch.float32)
             vs = part(v.v_scale, 4 * H).view(torch.float32)

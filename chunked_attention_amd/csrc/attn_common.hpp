@@ -37,7 +37,7 @@ static_assert(kWaves * kQW == kBq, "row = waves x queries per wave");
 
 struct SegArg {
   const unsigned char* k;   // [H][pitch][d]
-  const unsigned char* vt;  // [H][d][pitch]
+  const unsigned char* vt;  // [H][pitch/T][d][T], T = 32 (bf16) or 64 (fp8) keys
   const float* ks;          // [H] K scales (fp8 rings)
   const float* vs;          // [H] V scales (fp8 rings)
   int rows;

@@ -133,15 +133,16 @@ void attn_fwd_bf16(const AttnArgs a) {
       dma16(c.rk, kslot(DST) + blk * 1024, koff0 ^ (u << 6), sbase + blk * 1024);
     }
   };
+  // Vt is stored in 32-key tiles of D rows x 64 bytes: the step's tile is
+  // one contiguous 8 KB block and block blk of it holds rows 16*blk .. +15
+  const uint32_t voff = vrow * G::kVRow + vchunk;
   auto dma_v = [&](auto dst_tag, const TileCursor& c) {
     constexpr int DST = decltype(dst_tag)::value;
-    const uint32_t pitch2 = static_cast<uint32_t>(c.pitch) * 2;
-    const uint32_t voff = vrow * pitch2 + vchunk;
+    const uint32_t sbase = static_cast<uint32_t>(c.k0) * (2 * D);   // (k0 / 32) * 8 KB
 #pragma unroll
     for (int u = 0; u < G::kVInstr; ++u) {
       const int blk = wave * G::kVInstr + u;
-      dma16(c.rv, vslot(DST) + blk * 1024, voff,
-            static_cast<uint32_t>(blk) * 16 * pitch2 + static_cast<uint32_t>(c.k0) * 2);
+      dma16(c.rv, vslot(DST) + blk * 1024, voff, sbase + blk * 1024);
     }
   };
 

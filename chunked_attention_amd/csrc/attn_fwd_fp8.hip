@@ -148,15 +148,16 @@ void attn_fwd_fp8(const AttnArgs a) {
       dma16(c.rk, kslot(DST) + blk * 1024, koff[u], sbase + blk * 1024);
     }
   };
+  // Vt is stored in 64-key tiles of D rows x 64 bytes: the tile is one
+  // contiguous block and block blk of it holds rows 16*blk .. +15
+  const uint32_t voff = static_cast<uint32_t>(vrow) * 64 + vlog * 16;
   auto dma_v = [&](auto dst_tag, const TileCursor& c) {
     constexpr int DST = decltype(dst_tag)::value;
-    const uint32_t pitch = static_cast<uint32_t>(c.pitch);
-    const uint32_t voff = static_cast<uint32_t>(vrow) * pitch + vlog * 16;
+    const uint32_t sbase = static_cast<uint32_t>(c.k0) * D;   // (k0 / 64) * D * 64 bytes
 #pragma unroll
     for (int u = 0; u < G::kVInstr; ++u) {
       const int blk = wave * G::kVInstr + u;
-      dma16(c.rv, vslot(DST) + blk * 1024, voff,
-            static_cast<uint32_t>(blk) * 16 * pitch + static_cast<uint32_t>(c.k0));
+      dma16(c.rv, vslot(DST) + blk * 1024, voff, sbase + blk * 1024);
     }
   };
 

@@ -1,7 +1,9 @@
 // K1: fused cache write.  Moves a chunk's K/V from the caller's token-major
 // layout [rows][H][d] into a ring slot: K head-major [H][pitch][d] and V
-// transposed per head [H][d][pitch] (the layout the attention kernel's PV
-// product reads), zero-filling the padded rows.  Within every group of 16
+// transposed per head and tiled by the attention kernel's step, [H][pitch/T]
+// [d][T] with T = 32 keys (bf16) or 64 (fp8), so that the V operand of one
+// step is one contiguous 8 KB block, as the K operand is; padded rows are
+// zero-filled.  Within every group of 16
 // keys the bf16 V columns are stored in the order kappa (swap of key-index
 // bits 2 and 3), which is the order in which the attention kernel's score
 // accumulator hands keys to the PV product.  The fp8 variant quantises to
@@ -76,7 +78,8 @@ __global__ __launch_bounds__(kThreads) void cache_write_bf16(
     dst[3] = vv.w;
   }
   __syncthreads();
-  // transposed store: row dd of Vt gets 64 consecutive keys (8 chunks of 8)
+  // transposed store: the block's 64 keys are two 32-key tiles; row dd of
+  // tile b gets its 32 keys (4 chunks of 8)
   for (int c = tid; c < D * 8; c += kThreads) {
     const int dd = c / 8;
     const int ch = c % 8;
@@ -87,7 +90,9 @@ __global__ __launch_bounds__(kThreads) void cache_write_bf16(
       const uint32_t hi = vtile[kappa(ch * 8 + 2 * j + 1) * kLdsPitch + dd];
       w[j] = lo | (hi << 16);
     }
-    st16(vtd + (static_cast<size_t>(h) * D + dd) * pitch + r0 + ch * 8,
+    const int tile = (r0 >> 5) + (ch >> 2);
+    st16(vtd + static_cast<size_t>(h) * D * pitch + (static_cast<size_t>(tile) * D + dd) * 32 +
+             (ch & 3) * 8,
          make_uint4(w[0], w[1], w[2], w[3]));
   }
 }
@@ -229,7 +234,8 @@ __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
     vdst[1] = vc[1];
   }
   __syncthreads();
-  // transposed store: row dd of Vt gets 64 consecutive keys (4 chunks of 16)
+  // transposed store: the block is one 64-key tile; row dd gets its 64
+  // keys (4 chunks of 16)
   for (int c = tid; c < D * 4; c += kThreads) {
     const int dd = c / 4;
     const int ch = c % 4;
@@ -242,7 +248,8 @@ __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
         x |= static_cast<uint32_t>(vtile[pi64(ch * 16 + 4 * j + b) * kLdsPitch + dd]) << (8 * b);
       w[j] = x;
     }
-    st16(vtd + (static_cast<size_t>(h) * D + dd) * pitch + r0 + ch * 16,
+    st16(vtd + static_cast<size_t>(h) * D * pitch + (static_cast<size_t>(r0 >> 6) * D + dd) * 64 +
+             ch * 16,
          make_uint4(w[0], w[1], w[2], w[3]));
   }
 }

@@ -44,7 +44,7 @@ struct CacheWriteDesc {
   int head_dim = 0;
   int kv_dtype = KVC_KV_BF16;
   void* k_dst = nullptr;       // [H][pitch][d]
-  void* vt_dst = nullptr;      // [H][d][pitch]
+  void* vt_dst = nullptr;      // [H][pitch/T][d][T], T = 32 (bf16) or 64 (fp8)
   float* k_scale = nullptr;    // [H] (fp8)
   float* v_scale = nullptr;    // [H] (fp8)
   float* scratch = nullptr;    // fp8: float32 [2][H][pitch/kTileKeys] partial amax
@@ -54,7 +54,7 @@ struct CacheWriteDesc {
 // One logical segment of the visible KV, in device terms.
 struct AttnSegment {
   const void* k = nullptr;      // [H][pitch][d]
-  const void* vt = nullptr;     // [H][d][pitch]
+  const void* vt = nullptr;     // [H][pitch/T][d][T], T = 32 (bf16) or 64 (fp8)
   const float* k_scale = nullptr;
   const float* v_scale = nullptr;
   int rows = 0;

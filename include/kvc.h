@@ -108,10 +108,13 @@ typedef struct kvc_ring kvc_ring;   /* opaque host handle */
  * slot) and one slot for the s source rows (none if s = 0).  A slot of R rows stores,
  * with P = R rounded up to KVC_TILE_KEYS and e = 2 (bf16) or 1 (fp8) bytes:
  *   K  [H][P][d]  (key-major)        -- rows >= R are zero
- *   Vt [H][d][P]  (value, transposed) -- columns permuted within tiles:
+ *   Vt [H][P/T][d][T]  (value, transposed in tiles of T keys: T = 32 for
+ *                 bf16 rings, 64 for fp8 rings; tile b row j is feature j
+ *                 of keys T*b .. T*b+T-1, so one attention step's values are
+ *                 one contiguous block) -- columns permuted within tiles:
  *                 bf16 rings: column p holds key kappa(p), where kappa swaps
  *                 bits 2 and 3 of the index (keys permuted within each group
- *                 of 16); fp8 rings: column 64*b + p (p < 64) holds key
+ *                 of 16); fp8 rings: column p (p < 64) of tile b holds key
  *                 64*b + pi(p), pi(p) = ((p & 0x1C) << 1) | ((p & 0x20) >> 3)
  *                 | (p & 3).  Columns of keys >= R are zero.
  *   scales float32 [2][H] (K then V; fp8 rings only)
@@ -312,7 +315,7 @@ kvc_status kvc_get_segments(const kvc_ring* ring, kvc_segment* out, int32_t cap,
 
 typedef struct kvc_slot_view {
   void* k;              /* K  [H][pitch][d] */
-  void* vt;             /* Vt [H][d][pitch], columns permuted (kappa or pi, see above) */
+  void* vt;             /* Vt [H][pitch/T][d][T], columns permuted (kappa or pi, see above) */
   float* k_scale;       /* [H] (fp8 rings; NULL for bf16) */
   float* v_scale;       /* [H] */
   int32_t rows;         /* valid rows */

@@ -65,7 +65,8 @@ def test_cache_write_fp8_is_bit_exact(H, d, n, m):
         key = (p // 64) * 64 + pi64(p % 64)
         vpad = np.zeros((P, H, d), np.uint8)
         vpad[:rows] = vc
-        assert np.array_equal(Vt, vpad[key].transpose(1, 2, 0))
+        # stored in 64-key tiles: [H][P/64][d][64]
+        assert np.array_equal(Vt, vpad[key].reshape(P // 64, 64, H, d).transpose(2, 0, 3, 1))
 
 
 # Peaky inputs (logit std ~4: a few keys carry almost all the weight) are not

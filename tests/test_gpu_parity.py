@@ -48,7 +48,8 @@ def test_cache_write_bf16_is_bit_exact(H, d, n, m):
         kappa = (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1)
         vpad = torch.zeros(P, *vv.shape[1:], dtype=vv.dtype)
         vpad[:rows] = vv
-        expect = vpad[kappa].permute(1, 2, 0).contiguous()
+        # stored in 32-key tiles: [H][P/32][d][32]
+        expect = vpad[kappa].view(P // 32, 32, *vv.shape[1:]).permute(2, 0, 3, 1).contiguous()
         assert torch.equal(Vt.view(torch.int16), expect.view(torch.int16))
         assert (K[:, rows:].view(torch.int16) == 0).all()
 

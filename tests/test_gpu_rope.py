@@ -56,12 +56,13 @@ def test_cache_write_rope_bit_exact(H, d, n, m, s, dtype):
             assert torch.equal(K.cpu()[:, :rows].view(torch.int16),
                                krot.permute(1, 0, 2).contiguous().view(torch.int16))
             # V is not rotated: its plane holds the plain values
-            p = torch.arange(Vt.shape[2])
+            P = Vt.shape[1] * Vt.shape[3]
+            p = torch.arange(P)
             kappa = (p & ~0xC) | ((p & 4) << 1) | ((p & 8) >> 1)
-            vpad = torch.zeros(Vt.shape[2], H, d, dtype=torch.bfloat16)
+            vpad = torch.zeros(P, H, d, dtype=torch.bfloat16)
             vpad[:rows] = vv
-            assert torch.equal(Vt.cpu().view(torch.int16),
-                               vpad[kappa].permute(1, 2, 0).contiguous().view(torch.int16))
+            expect = vpad[kappa].view(P // 32, 32, H, d).permute(2, 0, 3, 1).contiguous()
+            assert torch.equal(Vt.cpu().view(torch.int16), expect.view(torch.int16))
         else:
             codes, scales = O3.quantize_segment(krot.float().numpy())
             assert np.array_equal(ks.cpu().numpy().view(np.uint32), scales.view(np.uint32))
