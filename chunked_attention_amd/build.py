@@ -35,6 +35,13 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+# Per-source extra flags.  The attention kernels are scheduled with LLVM's
+# max-memory-clause strategy: on MI355X it gave the bf16 kernel a schedule
+# 1.9% faster than the default one (fp8 kernel 0.5%), same results bit for bit.
+SOURCE_FLAGS = {
+    "attn_fwd.hip": ["-mllvm", "--amdgpu-sched-strategy=max-memory-clause"],
+    "attn_fwd_fp8.hip": ["-mllvm", "--amdgpu-sched-strategy=max-memory-clause"],
+}
 
 
 def _run(cmd: list[str], verbose: bool, cwd: str | None = None) -> None:
@@ -63,7 +70,8 @@ def build(verbose: bool = False, save_temps: str | None = None) -> str:
     jobs = []
     for src in hip_sources():
         obj = os.path.join(objdir, src + ".o")
-        cmd = [HIPCC, *HIP_FLAGS, f"-I{INCLUDE}", "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), f"-I{INCLUDE}", "-c",
+               os.path.join(CSRC, src), "-o", obj]
         cwd = None
         if save_temps:
             cwd = os.path.abspath(save_temps)
