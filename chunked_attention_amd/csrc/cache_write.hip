@@ -111,6 +111,24 @@ __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
   if (b != b) r = (r & 0x00FFu) | (((__float_as_uint(b) >> 24) & 0x80u) | 0x7Fu) << 8;
   return r;
 }
+// x / s for the quantiser, from r = 1/s (correctly rounded): y = x r, the
+// residual x - s y in one fused multiply-add, and one correction step y +
+// r (x - s y), with the sign of x (so that -0 stays -0).  This is not always
+// the correctly rounded quotient (the residual can underflow for tiny x), but
+// its E4M3 code is: an exhaustive check on MI355X over every bf16 x with
+// |x| <= amax and every bf16 amax found different codes only for amax below
+// 2^-104.  The caller uses it for scales s >= 2^-108 (amax >= 2^-100) and
+// finite; anything else takes the exact division.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+#pragma clang fp contract(off)
+  const float y = x * r;
+  const float e = fmaf(-s, y, x);
+  return copysignf(fmaf(e, r, y), x);
+}
+__device__ __forceinline__ bool fast_scale(float s) {
+  return s >= 0x1p-108f && s <= 0x1p+120f;
+}
+
 // Pass 1: per (head, 64-row block) largest magnitude of K and of V.
 
 template <int D>
@@ -203,6 +221,12 @@ __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
   }
   __syncthreads();
   const float sk = sc[0], sv = sc[1];
+  // x / s: reciprocal and one correction step when the scale allows it
+  // (uniform per head), else the correctly rounded division
+  const bool fast = fast_scale(sk) && fast_scale(sv);
+  const float rk = __fdiv_rn(1.0f, sk), rv = __fdiv_rn(1.0f, sv);
+  auto qk = [&](float x) { return fast ? div_by_scale(x, sk, rk) : __fdiv_rn(x, sk); };
+  auto qv = [&](float x) { return fast ? div_by_scale(x, sv, rv) : __fdiv_rn(x, sv); };
 
   for (int c = tid; c < kRowsPerBlock * kChunks; c += kThreads) {
     const int row = c / kChunks;
@@ -218,10 +242,10 @@ __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
       const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t k01 = e4m3x2(__fdiv_rn(bf16_bits_to_float(kw[j] & 0xFFFFu), sk),
-                                    __fdiv_rn(bf16_bits_to_float(kw[j] >> 16), sk));
-        const uint32_t v01 = e4m3x2(__fdiv_rn(bf16_bits_to_float(vw[j] & 0xFFFFu), sv),
-                                    __fdiv_rn(bf16_bits_to_float(vw[j] >> 16), sv));
+        const uint32_t k01 = e4m3x2(qk(bf16_bits_to_float(kw[j] & 0xFFFFu)),
+                                    qk(bf16_bits_to_float(kw[j] >> 16)));
+        const uint32_t v01 = e4m3x2(qv(bf16_bits_to_float(vw[j] & 0xFFFFu)),
+                                    qv(bf16_bits_to_float(vw[j] >> 16)));
         kc[j >> 1] |= k01 << (16 * (j & 1));
         vc[j >> 1] |= v01 << (16 * (j & 1));
       }

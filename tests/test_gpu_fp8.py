@@ -254,3 +254,36 @@ def test_fp8_codes_of_crafted_values():
     got = K.cpu().numpy()[0, :rows].reshape(-1)
     want = O3.encode(k.float().numpy().reshape(-1))
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("exp", [-130, -110, -101, -100, -99, -60, 0, 20, 100])
+def test_fp8_codes_across_scale_ranges(exp):
+    # The quantiser divides by the scale through a reciprocal and one
+    # correction step when amax >= 2^-100 and the exact division otherwise;
+    # both must give O3's codes.  Segments with amax near 2^exp: every bf16
+    # mantissa at a spread of exponents below amax (including values that
+    # are subnormal after scaling), both signs, zeros.
+    rng = np.random.default_rng(1000 + exp)
+    d, rows = 128, 96
+    mant = np.arange(128, dtype=np.float64) / 128.0 + 1.0      # every bf16 mantissa
+    e = rng.integers(-40, 1, size=rows * d)                      # 2^-40 .. 2^0 below amax
+    x = np.ldexp(np.resize(mant, rows * d), e + exp - 1)
+    x *= np.where(rng.random(rows * d) < 0.5, -1.0, 1.0)
+    x[:3] = [0.0, -0.0, np.ldexp(1.0, exp)]                       # amax = 2^exp
+    k = torch.from_numpy(x.astype(np.float32).reshape(rows, 1, d)).to(torch.bfloat16)
+    v = torch.flip(k, dims=[0])
+    r = kv.Ring(1, d, 64, rows, 0, kv_dtype="fp8_e4m3")
+    r.cond(k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    K, Vt, ks, vs, n = r.slot_tensors(-1)
+    kc, ksc = O3.quantize_segment(k.float().numpy())
+    vc, vsc = O3.quantize_segment(v.float().numpy())
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), ksc.view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), vsc.view(np.uint32))
+    assert np.array_equal(K.cpu().numpy()[:, :rows], kc.transpose(1, 0, 2))
+    P = Vt.shape[1] * Vt.shape[3]
+    p = np.arange(P)
+    key = (p // 64) * 64 + pi64(p % 64)
+    vpad = np.zeros((P, 1, d), np.uint8)
+    vpad[:rows] = vc
+    assert np.array_equal(Vt.cpu().numpy(), vpad[key].reshape(P // 64, 64, 1, d).transpose(2, 0, 3, 1))
