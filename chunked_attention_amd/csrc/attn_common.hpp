@@ -143,6 +143,12 @@ __device__ __forceinline__ void wait_vm_keep_lds_done() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
 }
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// s_waitcnt lgkmcnt(0) at the end of a step, right after the cursors moved:
+// a cursor that entered a new segment loaded its fields with scalar loads,
+// and scalar loads share the counter with LDS reads.  Waiting here, where no
+// LDS read is in flight, keeps the compiler from waiting for all of the next
+// step's LDS reads at the first use of those fields.
+__device__ __forceinline__ void wait_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // LDS tiles are stored as rows of RB bytes in 16-byte chunks; logical chunk c
 // of row r sits at physical chunk swz_chunk<RB>(r, c) (an XOR, so the same

@@ -371,6 +371,7 @@ void attn_fwd_bf16(const AttnArgs a) {
         cursor_next<D, 2, kStep>(a, cj, tlast, h);
         cursor_next<D, 2, kStep>(a, cv, tlast, h);
         cursor_next<D, 2, kStep>(a, ck, tlast, h);
+        wait_scalar_loads();
       };
 
       int j = t0;

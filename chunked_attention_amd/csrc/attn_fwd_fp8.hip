@@ -407,6 +407,7 @@ void attn_fwd_fp8(const AttnArgs a) {
         cursor_next<D, 1, kBk>(a, cj, tlast, h);
         cursor_next<D, 1, kBk>(a, cv, tlast, h);
         cursor_next<D, 1, kBk>(a, ck, tlast, h);
+        wait_scalar_loads();
       };
 
       int j = t0;
