@@ -227,11 +227,11 @@ void attn_fwd_bf16(const AttnArgs a) {
 
     f32x16_t oacc[kDB];
     float m_ref = 0.f, m_seen = -INFINITY;
-    float l_tot = 0.f, le_tot = 0.f;
+    float l_tot = 0.f;
     bool track_max = false;
     const int tlast = t1 - 1;
     for (int pass = 0;; ++pass) {
-      float l_run = 0.f, l_exact = 0.f;
+      float l_run = 0.f;
       m_seen = -INFINITY;
 #pragma unroll
       for (int db = 0; db < kDB; ++db)
@@ -332,17 +332,6 @@ void attn_fwd_bf16(const AttnArgs a) {
           acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), ones, acc1, false);
         }
         l_run += acc0 + acc1;
-        if constexpr (kLse) {
-          // the log-sum-exp output wants the exact sum of the unrounded p
-          float p[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(sc[i], a.c, neg_m));
-#pragma unroll
-          for (int st = 8; st >= 1; st >>= 1)
-#pragma unroll
-            for (int i = 0; i < st; ++i) p[i] += p[i + st];
-          l_exact += p[0];
-        }
 
         // O^T += Vt . P^T over these 32 keys
 #pragma unroll
@@ -388,7 +377,6 @@ void attn_fwd_bf16(const AttnArgs a) {
       wait_dma();
 
       l_tot = xor32_sum(l_run);
-      le_tot = kLse ? xor32_sum(l_exact) : 0.f;
       if (pass + 1 >= kMaxPasses) break;
       if (track_max) {
         // the true max is known now: no p of the next pass exceeds 1
@@ -408,7 +396,10 @@ void attn_fwd_bf16(const AttnArgs a) {
         m_ref += __log2f(l_tot);
     }
 
-    finish_piece<D, kLse>(a, oacc, m_ref, l_tot, le_tot, r, h, qbase, first_piece, w, wave,
+    // the log-sum-exp output is that of the weights applied: reference +
+    // log of the same sum O is divided by (within ln(1 + 2^-8) of the sum
+    // of the unrounded p, each weight being rounded to bf16 once)
+    finish_piece<D, kLse>(a, oacc, m_ref, l_tot, l_tot, r, h, qbase, first_piece, w, wave,
                           lane, s_ticket, sp);
   }
 }

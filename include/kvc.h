@@ -177,7 +177,11 @@ kvc_status kvc_append_chunk(kvc_ring* ring, int32_t kind, const void* k, const v
  *        committed clean K/V; the current chunk and its source tokens use the
  *        staged K/V (phase STAGED) or the committed K/V (COMMITTED).
  *   lse  optional [H][n+s] float32 natural-log log-sum-exp of the scaled
- *        logits per query (NULL to skip).
+ *        logits per query (NULL to skip): that of the weights applied, i.e.
+ *        the log of the sum O was normalised by, each weight rounded to the
+ *        P type of the product (bf16, or E4M3 for fp8 rings) -- within
+ *        ln(1 + 2^-8) of the exact value for bf16 rings.  Merging partial
+ *        results by their lse is then exact for the O returned.
  * q may not alias o.  No concatenated KV is formed: the kernel walks the
  * cache slots in logical order.
  * Errors: KVC_E_INVAL (null/misaligned pointers), KVC_E_STATE (phase EMPTY,

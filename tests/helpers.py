@@ -11,6 +11,12 @@ from oracle import fp8 as O3
 
 BF16_MAX_ABS = 2e-2
 BF16_REL_L2 = 5e-3
+# lse of bf16 rings is that of the weights applied: reference + ln of the sum
+# of the bf16-rounded probabilities that O is divided by.  Each weight is
+# rounded once to bf16 (8 significant bits, relative error <= 2^-8), so it is
+# within ln(1 + 2^-8) of the exact log-sum-exp; the slack covers the float32
+# arithmetic.
+LSE_BF16_BOUND = float(np.log1p(2.0 ** -8)) + 5e-5
 FP8_MAX_ABS = 6e-2
 
 
