@@ -17,10 +17,11 @@
 //      the same bits; four tokens per thread loaded at once);
 //   2. threshold mode: flag distances above tau^2.  Top-k mode: radix-select
 //      the keep-th largest distance over its 64-bit order-preserving key
-//      (eight 8-bit digit passes; one LDS histogram per wave, so colliding
-//      atomics stay within a wave, summed before one wave finds the bin),
-//      flag every larger key and, among keys equal to it, the lowest indices
-//      up to keep;
+//      (8-bit digits from the top; one LDS histogram per wave, so colliding
+//      atomics stay within a wave, summed before one wave finds the bin;
+//      done early once that bin holds exactly the keys still wanted), flag
+//      every larger key and, among keys equal to it, the lowest indices up
+//      to keep;
 //   3. compact: thread t owns tokens 16t .. 16t+15; a prefix sum of the flag
 //      counts (lane shuffles, then the waves' totals) gives each thread its
 //      output position.
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
   __shared__ unsigned whist[kWaves][256];   // per-wave histograms (less atomic contention)
   __shared__ unsigned hist[256];
   __shared__ unsigned long long s_prefix;
-  __shared__ int s_need;
+  __shared__ int s_need, s_cnt;
   const int tid = threadIdx.x;
   for (int i0 = tid; i0 < tokens; i0 += 4 * kThreads)
     distances<4>(zs, ze, tokens, channels, i0, vec, dist);
@@ -160,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
       // `need` = how many of the keys matching the prefix are still wanted
       unsigned long long prefix = 0, pmask = 0;
       int need = k;
+      bool whole_bin = false;   // every key matching the prefix is wanted
       const int wv = tid >> 6;
       for (int p = 56; p >= 0; p -= 8) {
         for (int b = tid; b < kWaves * 256; b += kThreads) (&whist[0][0])[b] = 0;
@@ -199,6 +201,7 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
             if (above < need && above + hb[q] >= need) {
               s_prefix = prefix | (static_cast<unsigned long long>(4 * l + q) << p);
               s_need = need - above;
+              s_cnt = hb[q];
             }
             above += hb[q];
           }
@@ -207,16 +210,24 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
         prefix = s_prefix;
         need = s_need;
         pmask |= 255ULL << p;
+        // the bin holds exactly the keys still wanted: all of them are in,
+        // so the lower digits cannot change the selection (for continuous
+        // distances this ends the select after two or three digits)
+        if (s_cnt == need) {
+          whole_bin = true;
+          break;
+        }
       }
       // larger keys are in; of the keys equal to the k-th, the first `need`
-      // by index
+      // by index (all of them when the select ended on a whole bin)
       unsigned eq = 0;
 #pragma unroll
       for (int j = 0; j < kPerThread; ++j) {
         const unsigned long long u = key[j];
         if (lo + j < tokens) {
-          if (u > prefix) flags |= 1u << j;
-          else if (u == prefix) eq |= 1u << j;
+          const unsigned long long um = u & pmask;
+          if (um > prefix || (whole_bin && um == prefix)) flags |= 1u << j;
+          else if (um == prefix) eq |= 1u << j;
         }
       }
       int unused;

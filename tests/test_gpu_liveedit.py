@@ -69,6 +69,21 @@ def test_edit_mask_ties_and_nan():
         check_mask(zs, ze, tau=tau)
 
 
+def test_edit_mask_deep_digits():
+    # distances 1 + (k 2^-20)^2 (k = token mod 256): equal in their top 40
+    # bits, so the top-k select runs through most digits before a bin holds
+    # exactly the keys still wanted; with 400 tokens, 144 values tie twice
+    tokens = 400
+    zs = torch.zeros(tokens, 2, dtype=torch.bfloat16)
+    ze = torch.zeros(tokens, 2, dtype=torch.float32)
+    ze[:, 0] = 1.0
+    ze[:, 1] = torch.tensor([(i % 256) * 2.0 ** -20 for i in range(tokens)])
+    ze = ze.to(torch.bfloat16)
+    assert torch.equal(ze[:, 1].float(), torch.tensor([(i % 256) * 2.0 ** -20 for i in range(tokens)]))
+    for keep in (1, 37, 144, 200, 257, 399):
+        check_mask(zs, ze, keep=keep)
+
+
 def test_edit_mask_rejects_bad_arguments():
     z = torch.zeros(4, 2, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(kv.KvcError):
