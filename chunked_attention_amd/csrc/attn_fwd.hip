@@ -6,8 +6,9 @@
 // tokens (discuss.pytorch.kr "JoyAI-Video-Edit 소개", chunk-wise
 // autoregressive adaptation section: bidirectional within the chunk, causal
 // across chunks through a sliding window plus the first chunk as global sink;
-// architecture section: the token groups and the mask between them).  The visible set is never concatenated: the kernel walks the ring's
-// segment table (cache slots in logical order) tile by tile.
+// architecture section: the token groups and the mask between them).  The
+// visible set is never concatenated: the kernel walks the ring's segment
+// table (cache slots in logical order) tile by tile.
 //
 // Work: a "row" is 128 queries of one head; its keys are T steps of 32 keys
 // over all segments (a segment's last step is masked).  A workgroup runs one
@@ -31,13 +32,18 @@
 // attn_common.hpp) so the 16 lanes an LDS clock serves hit distinct bank
 // groups; the reads of one operand differ by an XOR of one per-lane offset.
 // K and Vt are copied from global memory straight into LDS (buffer_load ...
-// lds, scalar base and offset, per-lane 32-bit offset).
+// lds, scalar base and offset, per-lane 32-bit offset); the ring stores Vt in
+// 32-key tiles, so both operands of a step are contiguous 8 KB blocks.
 //
 // Software pipeline over steps of 32 keys, with K and Vt in rings of four
 // LDS slots each: while the softmax of step s runs on the VALU, the QK^T
-// MFMAs of step s+1 are issued, then the PV MFMAs of step s.  K copies run
-// four steps ahead and Vt copies three, so every copy has two steps to land;
-// one barrier per step.
+// MFMAs of step s+1 are issued, then the PV MFMAs of step s (scheduling
+// groups ask the compiler to put six softmax VALU instructions after each
+// QK^T MFMA).  K copies run four steps ahead and Vt copies three, so every
+// copy has two steps to land; one barrier per step.  The two waves sharing a
+// SIMD (one from each of the CU's workgroups) take turns at the higher issue
+// priority, step by step, so that neither workgroup runs ahead and leaves
+// the other to finish its range alone.
 //
 // Softmax in base 2 with a fixed reference per row piece: t = s*scale*log2(e)
 // and p = 2^(t - m_ref), where m_ref is the max of the piece's first 32 keys,
@@ -47,6 +53,8 @@
 // the piece again, with m_ref raised by log2 of that sum (then no p exceeds
 // 1), or, if a sum overflowed, once more tracking the true max first.  Below
 // 2^64 every p, every sum and every accumulator is finite in fp32 and bf16.
+// The row sum adds the bf16-rounded p the PV product uses, and the optional
+// log-sum-exp output is reference + log of that same sum.
 #include "attn_common.hpp"
 
 namespace kvc {
