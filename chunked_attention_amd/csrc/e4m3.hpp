@@ -8,18 +8,12 @@
 #include <cstdint>
 #include <cstring>
 
-#if defined(__HIPCC__)
-#define KVC_HD __host__ __device__
-#else
-#define KVC_HD
-#endif
-
 namespace kvc {
 
 // Nearest E4M3 code of a float32 (ties to the even code), saturating at
 // +-448; NaN gives 0x7F with the sign kept.  E4M3: 1 sign, 4 exponent bits
 // (bias 7), 3 mantissa bits, subnormal spacing 2^-9, largest finite 448.
-KVC_HD inline uint8_t e4m3_from_float(float y) {
+inline uint8_t e4m3_from_float(float y) {
   uint32_t bits;
   std::memcpy(&bits, &y, sizeof(bits));
   const uint32_t sign = (bits >> 24) & 0x80u;
