@@ -317,15 +317,25 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
     // arrived already, so this is a short wait), then merge in piece order
     // whoever merges, so the result is bitwise the same from run to run:
     // sum_i O_i 2^(m_i - m_max), starting from the first piece
+    // The wait is bounded: the pieces waited for have all arrived and only
+    // have their stores left.  Should the bound ever be reached, the merged
+    // row is NaN rather than silently missing a partial.  (The flag has a
+    // word of its own: other waves may still be reading s_ticket.)
+    __shared__ unsigned s_missing;
     if (tid == 0) {
+      unsigned missing = 1;
       for (int spin = 0; spin < (1 << 26); ++spin) {
         if (__hip_atomic_load(written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-            npieces - 1)
+            npieces - 1) {
+          missing = 0;
           break;
+        }
         __builtin_amdgcn_s_sleep(1);
       }
+      s_missing = missing;
     }
     __syncthreads();
+    const bool poisoned = s_missing != 0;
     float mmax = m_run;
     for (int ow = w_lo; ow <= w_hi; ++ow) {
       if (ow == w) continue;
@@ -368,8 +378,8 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
 #pragma unroll
     for (int db = 0; db < kDB; ++db) oacc[db] = acc[db];
     m_run = mmax;
-    l_tot = l_acc;
-    le_tot = le_acc;
+    l_tot = poisoned ? __builtin_nanf("") : l_acc;
+    le_tot = poisoned ? __builtin_nanf("") : le_acc;
     if (tid == 0) {
       __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(written, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
