@@ -101,3 +101,29 @@ def test_token_groups_fp8(dist):
         assert st["max_abs"] <= FP8_MAX_ABS, (t, st)
         worst = max(worst, st["rel_l2"])
     print(f"fp8 groups {dist}: worst rel-L2 {worst:.3e}")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8_e4m3"])
+def test_largest_window_uses_every_segment(kv_dtype):
+    # W = KVC_MAX_WINDOW with condition, reference and source tokens: from
+    # chunk W+1 on the segment table holds KVC_MAX_SEGMENTS entries (cond, ref,
+    # sink, W window chunks, current, source).  Ragged sizes; the last chunks
+    # are checked against the oracle.
+    W = kv.KVC_MAX_WINDOW
+    w = synth.Workload("maxwin", 2, 64, 40, 20, W, W + 4, seed=33, kv_dtype=kv_dtype,
+                       ref_tokens=10, source_tokens=12)
+    fp8 = kv_dtype != "bf16"
+    print(f"max window {kv_dtype}", flush=True)
+    run = StreamRun(synth.Stream(w, "baseline"), ring_for(w), fp8=fp8)
+    for t in range(w.chunks):
+        check = t >= W + 1
+        res, = run.chunk(t, check=check, lse=check and not fp8)
+        if check:
+            # cond + ref + sink + W window chunks + current + source
+            assert O1.kv_length(t, 20, 40, W, 10, 12) == 20 + 10 + 40 * (W + 2) + 12
+            o, ref, st = res
+            if fp8:
+                assert st["finite"] and st["max_abs"] <= FP8_MAX_ABS, (t, st)
+            else:
+                assert_bf16_parity(st, f"max window t={t}")
+                assert st["lse_max_abs"] < LSE_BF16_BOUND, st
