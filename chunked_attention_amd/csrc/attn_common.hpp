@@ -119,6 +119,37 @@ __device__ __forceinline__ int owner_of(long long x, const Split& sp) {
   return static_cast<int>(((x + 1) * sp.nwg - 1) / sp.total);
 }
 
+// The pieces of workgroup w's range [xb, xe) of the flattened (row, step)
+// space, one per row it touches, taken whole rows first, then the last
+// piece, then the first (with two or fewer, last first).  For ranges over
+// several long rows: the partial first piece, taken first, would set the
+// workgroups out of step for the rest of the call; whole rows first keep the
+// workgroups that share a head on the same keys at once.  get(i) gives the
+// i-th piece's row, its steps [t0, t1) and whether it holds the range's first
+// step (the partial slot it uses when its row is split); the merge does not
+// depend on the order.
+struct RowsFirst {
+  int rb, np, tf, tl, ntiles;
+  __device__ __forceinline__ RowsFirst(long long xb, long long xe, int nt) : ntiles(nt) {
+    rb = static_cast<int>(xb / nt);
+    const int rl = xe > xb ? static_cast<int>((xe - 1) / nt) : rb - 1;
+    np = rl - rb + 1;
+    tf = static_cast<int>(xb - static_cast<long long>(rb) * nt);
+    tl = static_cast<int>(xe - static_cast<long long>(rl) * nt);
+  }
+  __device__ __forceinline__ void get(int i, int& r, int& t0, int& t1, bool& first) const {
+    const int pi = np <= 2 ? np - 1 - i : (i < np - 2 ? i + 1 : (i == np - 2 ? np - 1 : 0));
+    r = rb + pi;
+    t0 = pi == 0 ? tf : 0;
+    t1 = pi == np - 1 ? tl : ntiles;
+    first = pi == 0;
+  }
+};
+// whether whole rows first pays: ranges that span more than two rows
+inline bool rows_first(long long total, int nwg, int ntiles) {
+  return total > 2LL * ntiles * nwg;
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // buffer resource over `bytes` bytes at `base` (raw buffer: stride 0, offsets

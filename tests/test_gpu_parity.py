@@ -111,6 +111,22 @@ def test_720p_steady_chunk_all_heads():
     assert O1.kv_length(4, 256, 1620, 3) == 8356
 
 
+def test_three_frame_chunk_whole_rows_first():
+    # the full LiveEdit chunk on the plain call: 4860 queries, 40 heads x 128,
+    # W = 3 (24556 keys from chunk 4).  1520 rows of 384 steps over 512
+    # workgroups: every range spans three or four rows, so the pieces run
+    # whole rows first, then the last, then the first.  Oracle on 3 heads.
+    w = synth.WORKLOADS["edit3"]
+    heads = [0, 21, 39]
+    run = StreamRun(synth.Stream(w, "baseline"), ring_for(w), heads=heads)
+    for t in range(4):
+        run.chunk(t, check=False)
+    (o, ref, st), = run.chunk(4, lse=True)
+    assert_bf16_parity(st, "edit3 t=4 sampled heads")
+    assert st["lse_max_abs"] < LSE_BF16_BOUND, st
+    assert O1.kv_length(4, 256, 4860, 3) == 24556
+
+
 @pytest.mark.parametrize("where", ["cond", "current"])
 @pytest.mark.parametrize("shift", [30.0, -30.0, 80.0, -80.0])
 def test_segment_offset_stress(where, shift):
