@@ -200,13 +200,14 @@ def run_stream_bench(w, args, device, flat: bool):
     per_step = w.steps * w.layers * 4 + w.layers * 4 + 1
     pool_ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps * per_step + 2)]
     ev_iter = iter(pool_ev)
-    attn_events, write_events, step_events, mask_events = [], [], [], []
+    attn_events, write_events, step_spans, mask_events = [], [], [], []
     kv_len = [0]        # keys attended by the timed calls (largest)
 
-    # Timed chunks record exactly one event between consecutive launches (an
-    # event record itself takes a few microseconds on the stream): `last` is
-    # the event that closes the previous launch and opens the next, carried
-    # from one timed chunk to the next (the first one starts at `start`).
+    # An instrumented chunk records exactly one event between consecutive
+    # launches (an event record itself takes a few microseconds on the
+    # stream): `last` is the event that closes the previous launch and opens
+    # the next; the chunk opens at `carry["last"]` (or a fresh event) and
+    # leaves its closing event there.
     carry = {"last": None}
 
     def chunk(t: int, timed: bool):
@@ -217,7 +218,7 @@ def run_stream_bench(w, args, device, flat: bool):
             if last is None:
                 last = next(ev_iter)
                 last.record(stream)
-            step_events.append(last)
+            opening = last
         if keep is not None:
             # LiveEdit: this chunk's active rows from the previous chunk's
             # latents, on the device (shared by every layer and step)
@@ -272,6 +273,8 @@ def run_stream_bench(w, args, device, flat: bool):
                     attend(r, inp.q[c][0], outs[li & 1])
             r.evict()
         carry["last"] = last
+        if timed:
+            step_spans.append((opening, last))
 
     def clock_warmup(t: int) -> int:
         # The GPU raises its shader clock over tens of milliseconds of
@@ -317,11 +320,20 @@ def run_stream_bench(w, args, device, flat: bool):
                 t += 1
         torch.cuda.synchronize()
         t_first = t
+        # every `every`-th timed chunk is instrumented with per-launch events;
+        # the others run as a caller runs them (the throughput is start to end
+        # over all of them)
+        every = 1 if flat else max(1, args.sample_every)
         start.record(stream)
         carry["last"] = start
         h0 = time.perf_counter()
-        for _ in range(steps):
-            chunk(t, True)
+        for i in range(steps):
+            if i % every == 0:
+                if i:
+                    carry["last"] = None
+                chunk(t, True)
+            else:
+                chunk(t, False)
             t += 1
         end.record(stream)
         host_s = time.perf_counter() - h0   # enqueue time (the GPU runs behind)
@@ -330,8 +342,7 @@ def run_stream_bench(w, args, device, flat: bool):
         gc.enable()
     tele_after = gpu_telemetry() if flat else None
     total_ms = start.elapsed_time(end)
-    step_ms = [step_events[i].elapsed_time(step_events[i + 1])
-               for i in range(len(step_events) - 1)] + [step_events[-1].elapsed_time(end)]
+    step_ms = [a.elapsed_time(b) for a, b in step_spans]
     res = {
         "host_ms_per_step": host_s * 1e3 / steps,
         "ms_per_step": total_ms / steps,
@@ -341,6 +352,7 @@ def run_stream_bench(w, args, device, flat: bool):
         "write_ms": [a.elapsed_time(b) for a, b in write_events],
         "mask_ms": [a.elapsed_time(b) for a, b in mask_events],
         "step_ms": step_ms,
+        "sample_every": every,
         "kv_len": kv_len[0],
         "first_chunk": t_first,
         "last_chunk": t - 1,
@@ -439,6 +451,9 @@ def main() -> int:
     ap.add_argument("--pool", type=int, default=16, help="distinct input chunks uploaded")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sample-every", type=int, default=4, metavar="N",
+                    help="record per-launch events on every N-th timed step (1: all; the "
+                         "long-stream mode records every chunk)")
     ap.add_argument("--window", type=int, default=None,
                     help="override the config's window W (e.g. the long stream at W=3)")
     ap.add_argument("--clean-pass", action="store_true",
@@ -547,6 +562,8 @@ def main() -> int:
         "cache_write_gbps": round(write_bytes / (write_us * 1e-6) / 1e9, 1),
         "edit_mask_median_us": (round(statistics.median(r["mask_ms"]) * 1e3, 2)
                                 if r["mask_ms"] else None),
+        "instrumented_steps": len(steps_ms),
+        "sample_every": r["sample_every"],
         "step_ms_median": round(med, 4),
         "step_ms_max_dev_pct": dev(steps_ms, med),
         "step_ms_p99": round(sorted(steps_ms)[min(len(steps_ms) - 1, int(0.99 * len(steps_ms)))], 4),
@@ -558,8 +575,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": f"attn_fwd_{'fp8' if fp8 else 'bf16'}<{w.head_dim},false,"
-                      f"{'true' if args.rope else 'false'}>",
+            "kernel": f"attn_fwd_{'fp8' if fp8 else 'bf16'} (d={w.head_dim}, no lse"
+                      f"{', rope' if args.rope else ''})",
             "per_launch_flops": flops,
         },
     }
