@@ -2,6 +2,10 @@
 
     python -m chunked_attention_amd.profiling stats DIR --cmd "..." --out FILE.md
         kernel statistics (--kernel-trace --stats --output-format csv run in DIR)
+    python -m chunked_attention_amd.profiling counters DIR [DIR ...] --cmd "..." [--cmd ...] \\
+        --flops F --out FILE.md
+        SQ / TCC / GRBM counters of the attention kernel (one --pmc run per
+        DIR), per dispatch, with the MFMA-busy fraction and its algorithmic part
     python -m chunked_attention_amd.profiling traffic --fetch DIR --write DIR \\
         --calib-mib M --cmd-fetch "..." --cmd-write "..." --out FILE.json --md FILE.md
         HBM bytes per launch of the attention kernel from two counter runs
@@ -107,6 +111,70 @@ def _counter(dirname: str, counter: str):
     return [per[d] for d in sorted(per)]
 
 
+def _dispatches(dirname: str):
+    """{dispatch id: (kernel name, duration ns, {counter: value summed over instances})}"""
+    path = _one(dirname, "*counter_collection.csv")
+    per = {}
+    for r in csv.DictReader(open(path)):
+        did = int(r["Dispatch_Id"])
+        if did not in per:
+            per[did] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {})
+        c = per[did][2]
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return per
+
+
+# gfx950: 256 CUs in 8 XCDs, 4 SIMDs per CU; a 32x32x16 bf16 MFMA keeps its
+# SIMD's matrix pipe busy 32 cycles for 32768 FLOPs
+CUS, XCDS, SIMDS = 256, 8, 4
+BF16_FLOPS_PER_SIMD_CYCLE = 1024
+
+
+def counters_md(dirs, cmds, steady: int, flops: float, workload: str) -> str:
+    vals, durs = {}, []
+    for d in dirs:
+        attn = [v for _, v in sorted(_dispatches(d).items()) if ATTN in v[0]][-steady:]
+        if not attn:
+            raise SystemExit(f"no attention dispatches in {d}")
+        durs += [dur for _, dur, _ in attn]
+        for name in attn[0][2]:
+            vals[name] = statistics.mean(c[name] for _, _, c in attn)
+    dur_s = statistics.mean(durs) * 1e-9
+    out = ["# Counters of the attention kernel (rocprofv3 --pmc)", "",
+           f"Workload: {workload}.  Each counter summed over its hardware instances and "
+           f"averaged over the last {steady} attention dispatches of its run; one run per "
+           f"counter set.", "", "Commands (from the repository root):", "", "```", *cmds,
+           "```", "", "| counter | per dispatch |", "|---|---|"]
+    out += [f"| {k} | {v:,.0f} |" for k, v in sorted(vals.items())]
+    out += ["", f"Mean dispatch time in these runs: {dur_s * 1e6:.1f} us.", ""]
+    derived = []
+    if "GRBM_GUI_ACTIVE" in vals:
+        cycles = vals["GRBM_GUI_ACTIVE"] / XCDS
+        derived.append(f"- GPU cycles per dispatch: GRBM_GUI_ACTIVE / {XCDS} XCDs = "
+                       f"{cycles:,.0f}, i.e. a {cycles / dur_s / 1e9:.2f} GHz clock over the "
+                       f"dispatch time.")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+            simd_cycles = cycles * CUS * SIMDS
+            busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"]
+            derived.append(f"- Matrix pipes busy: SQ_VALU_MFMA_BUSY_CYCLES / ({CUS} CUs x "
+                           f"{SIMDS} SIMDs x cycles) = {100 * busy / simd_cycles:.1f}%.")
+            if flops:
+                need = flops / BF16_FLOPS_PER_SIMD_CYCLE
+                derived.append(f"- The algorithmic {flops / 1e9:.2f} GFLOP need {need:,.0f} "
+                               f"busy SIMD-cycles at {BF16_FLOPS_PER_SIMD_CYCLE} FLOP each: "
+                               f"{100 * need / busy:.1f}% of the busy cycles (the rest: "
+                               f"padded tiles and rows).")
+    if "SQ_LDS_BANK_CONFLICT" in vals and vals.get("SQ_INSTS_LDS"):
+        derived.append(f"- LDS bank-conflict cycles per LDS instruction: "
+                       f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_INSTS_LDS']:.3f}.")
+    if "TCC_HIT_sum" in vals and "TCC_MISS_sum" in vals:
+        h, m = vals["TCC_HIT_sum"], vals["TCC_MISS_sum"]
+        derived.append(f"- L2 hit rate: {100 * h / (h + m):.1f}%.")
+    if derived:
+        out += ["Derived:", ""] + derived + [""]
+    return "\n".join(out)
+
+
 def traffic(fetch_dir, write_dir, calib_mib, steady):
     calib_bytes = calib_mib << 20
     res = {}
@@ -135,6 +203,13 @@ def main(argv=None):
     a.add_argument("--out", required=True)
     a.add_argument("--steady", type=int, default=0,
                    help="also report the mean of the last N attention dispatches")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--cmd", action="append", required=True)
+    c.add_argument("--steady", type=int, default=3)
+    c.add_argument("--flops", type=float, default=0.0, help="algorithmic FLOPs per call")
+    c.add_argument("--workload", default="720p steady chunk (8356 keys)")
+    c.add_argument("--out", required=True)
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -148,6 +223,10 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.what == "stats":
         open(args.out, "w").write(stats_md(args.dir, args.cmd, args.steady))
+        return 0
+    if args.what == "counters":
+        open(args.out, "w").write(counters_md(args.dirs, args.cmd, args.steady, args.flops,
+                                              args.workload))
         return 0
     res, total = traffic(args.fetch, args.write, args.calib_mib, args.steady)
     sha = kernel_code_digest()
