@@ -102,6 +102,35 @@ __device__ __forceinline__ Split make_split(const AttnArgs& a) {
   const long long by_size = max(1LL, total * a.step_keys / kMinPieceKeys);
   return Split{total, nqt, nq, static_cast<int>(min(static_cast<long long>(a.nwg), by_size))};
 }
+// Workgroups for a split of `rows` rows of `steps` steps over at most `cap`.
+// When the rows fit, the largest multiple m of the row count within cap:
+// range w starts at step w * rows * steps / m, a row start whenever w is a
+// multiple of m / rows, so every range lies inside one row and no workgroup
+// pays the fixed cost of a second piece (its opening copies, a partial or a
+// merge; about kPieceCostSteps steps) while the others have one.  Taken when
+// the longer ranges cost fewer steps than that: rows * steps * (1/m - 1/cap)
+// <= kPieceCostSteps.
+constexpr long long kPieceCostSteps = 6;
+__device__ __forceinline__ int split_workgroups(int rows, int steps, int cap) {
+  if (rows > 0 && rows <= cap) {
+    const int m = cap / rows * rows;
+    if (static_cast<long long>(rows) * steps * (cap - m) <=
+        kPieceCostSteps * static_cast<long long>(m) * cap)
+      return m;
+  }
+  return cap;
+}
+// The split of an active-row call (its own kernel instance; a.qcount is
+// set): from the device-side count, with ranges inside one row where that
+// costs few steps.
+__device__ __forceinline__ Split make_split_active(const AttnArgs& a) {
+  const int nq = min(max(*a.qcount, 0), a.n);
+  const int nqt = (nq + kBq - 1) / kBq;
+  const long long total = static_cast<long long>(a.heads) * nqt * a.ntiles;
+  const long long by_size = max(1LL, total * a.step_keys / kMinPieceKeys);
+  const int cap = static_cast<int>(min(static_cast<long long>(a.nwg), by_size));
+  return Split{total, nqt, nq, split_workgroups(a.heads * nqt, a.ntiles, cap)};
+}
 // row of q / o / lse that query qi of the call stands for, or -1 if none
 // (past the active count, or an index outside the tensors)
 __device__ __forceinline__ int query_row(const AttnArgs& a, const Split& sp, int qi) {

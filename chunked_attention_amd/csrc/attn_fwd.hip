@@ -81,7 +81,7 @@ struct Geo {
   static_assert(kKInstr >= 1 && kVInstr >= 1 && kKInstr == kVInstr, "copy counts");
 };
 
-template <int D, bool kLse, bool kRope, bool kRowsFirst>
+template <int D, bool kLse, bool kRope, bool kRowsFirst, bool kActive>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_bf16(const AttnArgs a) {
   using G = Geo<D>;
@@ -194,7 +194,7 @@ void attn_fwd_bf16(const AttnArgs a) {
     return xor32_max(mx) * a.c;
   };
 
-  const Split sp = make_split(a);
+  const Split sp = kActive ? make_split_active(a) : make_split(a);
   if (w >= sp.nwg) return;
   // one piece: steps [t0, t1) of row r; first_piece if it holds the first
   // step of this workgroup's range (the partial slot it uses if split)
@@ -436,17 +436,25 @@ kvc_status launch_bf16(const AttnDesc& d, hipStream_t stream) {
   if (st != KVC_OK) return st;
   if (!d.workspace_ready) launch_fill_u32(a.counters, 2 * a.nrows, 0u, stream);
   const dim3 grid(a.nwg), block(kThreads);
-  // whole rows first only on the plain call over long rows (RoPE and
-  // active-row calls keep one instance each)
-  if (a.qrope) {
-    if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16<D, false, true, false>), grid, block, 0, stream, a);
-  } else if (!a.qcount && rows_first(a.total, a.nwg, a.ntiles)) {
-    if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, false, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16<D, false, false, true>), grid, block, 0, stream, a);
+  // active-row calls have instances of their own (their split is taken in
+  // the kernel); whole rows first only on the plain call over long rows
+  if (a.qcount) {
+    if (a.qrope) {
+      if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, true, false, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16<D, false, true, false, true>), grid, block, 0, stream, a);
+    } else {
+      if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, false, false, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16<D, false, false, false, true>), grid, block, 0, stream, a);
+    }
+  } else if (a.qrope) {
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, true, false, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16<D, false, true, false, false>), grid, block, 0, stream, a);
+  } else if (rows_first(a.total, a.nwg, a.ntiles)) {
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, false, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16<D, false, false, true, false>), grid, block, 0, stream, a);
   } else {
-    if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, false, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16<D, false, false, false>), grid, block, 0, stream, a);
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, false, false, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_bf16<D, false, false, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_DEVICE;
 }

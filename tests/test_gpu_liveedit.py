@@ -204,6 +204,19 @@ def test_rows_attention_fp8():
     run_rows_stream(w, "baseline", (8, 12), 1, 16, keep_frac=0.3, fp8=True, lse=False)
 
 
+@pytest.mark.parametrize("keep_frac", [0.3, 0.1])
+def test_rows_attention_720p_chunk_row_aligned_split(keep_frac):
+    # 1620-token chunks, 40 heads x 128, W = 3: 486 (or 162) active rows make
+    # 160 (80) rows of 131 steps, which the active-row call splits over 480
+    # workgroups, three (six) to a row, each range inside one row.  Oracle on
+    # 3 heads at chunks 1 and 4 (8356 keys).
+    w = synth.WORKLOADS["720p"]
+    w = synth.Workload("720p", w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window,
+                       5, std=w.std, seed=w.seed)
+    run_rows_stream(w, "baseline", (30, 54), 1, 16, keep_frac=keep_frac, heads=[0, 17, 39],
+                    check_chunks={1, 4})
+
+
 def test_rows_attention_three_frame_chunks_sampled_heads():
     # the LiveEdit chunk: three latent frames of a 30x54 grid (4860 tokens),
     # 40 heads x 128, 256 condition tokens, W = 3, about 30% of rows active
