@@ -19,6 +19,15 @@
 // contiguous ranges (stream-K), so the whole GPU stays busy whatever R is;
 // the split and the merge of split rows live in attn_common.hpp.
 //
+// Instances (template flags): kLse (log-sum-exp output), kRope (q rotated at
+// its load), kRowsFirst (the plain call over ranges of more than two rows
+// walks a workgroup's pieces whole rows first; otherwise last first) and
+// kActive (active-row calls: the split is taken in the kernel from the
+// device-side row count, with ranges kept inside one row where that costs
+// few steps).  Each is its own instance so that the others' code stays as
+// it is: the kernel sits at the register limit, and code added for one case
+// moved the schedule of the rest.
+//
 // Per step and wave (32 keys x 32 queries), with 32x32x16 bf16 MFMAs (fp32
 // accumulate):
 //   S^T[32 keys x 32 q] = K_step . Q^T      A = K from LDS, B = Q in VGPRs
