@@ -87,7 +87,7 @@ __device__ __forceinline__ int pack8(float x, float y, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(x, y, old, kHigh);
 }
 
-template <int D, bool kLse, bool kRope>
+template <int D, bool kLse, bool kRope, bool kRowsFirst>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8(const AttnArgs a) {
   using G = Geo8<D>;
@@ -203,19 +203,9 @@ void attn_fwd_fp8(const AttnArgs a) {
 
   const Split sp = make_split(a);
   if (w >= sp.nwg) return;
-  // The pieces of this workgroup's range (one per row it touches) run last
-  // first: every workgroup then starts at the first step of a row, and the
-  // workgroups sharing a head walk its keys nearly in step, so one copy of
-  // each tile in L2 serves them all.
-  const long long xb = range_begin(w, sp);
-  for (long long e = range_begin(w + 1, sp); e > xb;) {
-    const int r = static_cast<int>((e - 1) / a.ntiles);
-    const long long row_start = static_cast<long long>(r) * a.ntiles;
-    const long long s0 = xb > row_start ? xb : row_start;
-    const int t0 = static_cast<int>(s0 - row_start);
-    const int t1 = static_cast<int>(e - row_start);
-    const bool first_piece = s0 == xb;
-    e = s0;
+  // one piece: tiles [t0, t1) of row r; first_piece if it holds the first
+  // tile of this workgroup's range (the partial slot it uses if split)
+  auto piece = [&](const int r, const int t0, const int t1, const bool first_piece) {
     const int h = r / sp.nqt;
     const int qbase = (r - h * sp.nqt) * kBq + wave * kQW;
 
@@ -438,6 +428,33 @@ void attn_fwd_fp8(const AttnArgs a) {
     const float l_tot = lacc[0];
     finish_piece<D, kLse>(a, oacc, m_ref, l_tot, l_tot, r, h, qbase, first_piece, w, wave, lane,
                           s_ticket, sp);
+  };
+
+  // The pieces of this workgroup's range (one per row it touches).
+  const long long xb = range_begin(w, sp);
+  if constexpr (kRowsFirst) {
+    // whole rows first, then the last piece, then the first
+    RowsFirst pieces(xb, range_begin(w + 1, sp), a.ntiles);
+    for (int i = 0; i < pieces.np; ++i) {
+      int r, t0, t1;
+      bool first_piece;
+      pieces.get(i, r, t0, t1, first_piece);
+      piece(r, t0, t1, first_piece);
+    }
+  } else {
+    // last first: every workgroup then starts at the first tile of a row,
+    // and the workgroups sharing a head walk its keys nearly in step, so one
+    // copy of each tile in L2 serves them all
+    for (long long e = range_begin(w + 1, sp); e > xb;) {
+      const int r = static_cast<int>((e - 1) / a.ntiles);
+      const long long row_start = static_cast<long long>(r) * a.ntiles;
+      const long long s0 = xb > row_start ? xb : row_start;
+      const int t0 = static_cast<int>(s0 - row_start);
+      const int t1 = static_cast<int>(e - row_start);
+      const bool first_piece = s0 == xb;
+      e = s0;
+      piece(r, t0, t1, first_piece);
+    }
   }
 }
 
@@ -450,12 +467,17 @@ kvc_status launch_fp8_d(const AttnDesc& d, hipStream_t stream) {
     if (!a.seg[s].ks || !a.seg[s].vs) return KVC_E_INVAL;
   if (!d.workspace_ready) launch_fill_u32(a.counters, 2 * a.nrows, 0u, stream);
   const dim3 grid(a.nwg), block(kThreads);
+  // whole rows first only on the plain call over long rows (RoPE and
+  // active-row calls keep one instance each)
   if (a.qrope) {
-    if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_fp8<D, false, true>), grid, block, 0, stream, a);
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_fp8<D, false, true, false>), grid, block, 0, stream, a);
+  } else if (!a.qcount && rows_first(a.total, a.nwg, a.ntiles)) {
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_fp8<D, false, false, true>), grid, block, 0, stream, a);
   } else {
-    if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_fp8<D, false, false>), grid, block, 0, stream, a);
+    if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, false, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((attn_fwd_fp8<D, false, false, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_DEVICE;
 }

@@ -141,6 +141,19 @@ def test_fp8_config_stream_sampled(dist):
         print(f"fp8 cfg {dist} t={t}: max-abs {st['max_abs']:.2e} rel-L2 {st['rel_l2']:.2e}")
 
 
+def test_fp8_three_frame_chunk_whole_rows_first():
+    # 4860-query chunks on an E4M3 ring (40 heads x 128, W = 3, 24556 keys
+    # from chunk 4): 1520 rows of 384 tiles over 512 workgroups, so the
+    # pieces run whole rows first.  Oracle on 3 heads at chunk 4.
+    w = fp8_workload(synth.WORKLOADS["edit3"], name="edit3-fp8")
+    heads = [0, 21, 39]
+    run = StreamRun(synth.Stream(w, "baseline"), fp8_ring(w), fp8=True, heads=heads)
+    for t in range(4):
+        run.chunk(t, check=False)
+    (o, ref, st), = run.chunk(4, lse=True)
+    check_fp8(st, "edit3 fp8 t=4")
+
+
 @pytest.mark.parametrize("where", ["cond", "current"])
 @pytest.mark.parametrize("shift", [30.0, -30.0, 80.0])
 def test_fp8_segment_offset_stress(where, shift):
