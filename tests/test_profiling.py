@@ -75,3 +75,32 @@ def test_counter_summary_derives_mfma_busy_and_its_algorithmic_share(tmp_path):
     assert "L2 hit rate: 90.0%." in md
     assert "Mean dispatch time in these runs: 100.0 us." in md
     assert "cmd a" in md and "cmd b" in md
+
+
+def test_kernel_stats_summary_and_steady_mean(tmp_path):
+    d = tmp_path / "s"
+    os.makedirs(d)
+    with open(d / "run_kernel_stats.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Name", "Calls", "TotalDurationNs", "AverageNs",
+                                          "MinNs", "MaxNs", "Percentage"])
+        w.writeheader()
+        w.writerow({"Name": ATTN_NAME, "Calls": 3, "TotalDurationNs": 600000,
+                    "AverageNs": 200000, "MinNs": 100000, "MaxNs": 300000, "Percentage": 90.0})
+        w.writerow({"Name": "void kvc::cache_write_bf16<128>(...)", "Calls": 6,
+                    "TotalDurationNs": 66000, "AverageNs": 11000, "MinNs": 10000,
+                    "MaxNs": 12000, "Percentage": 10.0})
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        # three attention calls (100, 300, 200 us) and a cache write between
+        for start, dur in ((0, 100000), (400000, 300000), (900000, 200000)):
+            w.writerow({"Kernel_Name": ATTN_NAME, "Start_Timestamp": start,
+                        "End_Timestamp": start + dur})
+        w.writerow({"Kernel_Name": "cache_write_bf16", "Start_Timestamp": 200000,
+                    "End_Timestamp": 211000})
+    md = P.stats_md(str(d), "the command", steady=2)
+    assert "the command" in md
+    assert "| attn_fwd_bf16<128, false, false, false> | 3 | 600.0 | 200.00 |" in md
+    assert "| cache_write | 6 | 66.0 | 11.00 |" in md
+    # the last two attention calls in time order: 300 and 200 us
+    assert "mean 250.00 us per call" in md
