@@ -218,12 +218,16 @@ def _attn_args(cfg: kvc_config, q, o, lse):
     nq = query_rows(cfg)
     _check_tokens(q, nq, cfg, "q")
     _check_tokens(o, nq, cfg, "o")
+    if o.device != q.device:
+        raise ValueError("q and o must be on the same device")
     lse_ptr = None
     if lse is not None:
-        if lse.dtype != torch.float32 or not lse.is_contiguous() or \
+        if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() or \
                 tuple(lse.shape) != (cfg.heads, nq):
-            raise ValueError("lse must be a contiguous float32 [heads, chunk_tokens + "
-                             "source_tokens] tensor")
+            raise ValueError("lse must be a contiguous float32 CUDA tensor [heads, "
+                             "chunk_tokens + source_tokens]")
+        if lse.device != q.device:
+            raise ValueError("lse must be on q's device")
         lse_ptr = lse.data_ptr()
     return ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(o.data_ptr()), ctypes.c_void_p(lse_ptr)
 

@@ -24,6 +24,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvc.so")
 HOST_LIB = os.path.join(BUILD, "libkvc_hostcheck.so")
+HOST_LIB_SAN = os.path.join(BUILD, "libkvc_hostcheck_san.so")
+# AddressSanitizer + UndefinedBehaviorSanitizer for the CPU test build of the
+# host logic (g++ only: no device code is built with them).  A process that
+# loads it must preload the ASan runtime (asan_runtime()).
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-fno-omit-frame-pointer", "-g"]
 
 HIP_SOURCES = ["cache_write.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "edit_mask.hip"]
 CPP_SOURCES = ["ring.cpp", "plan.cpp"]
@@ -92,25 +98,34 @@ def build(verbose: bool = False, save_temps: str | None = None) -> str:
     return LIB
 
 
-def build_host(verbose: bool = False) -> str:
-    """CPU-only library of the host logic (ring, ABI, plan, E4M3 encoder)
-    linked against the recording test launcher in tests/."""
+def build_host(verbose: bool = False, sanitize: bool = False) -> str:
+    """CPU-only library of the host logic (ring, ABI, plan) linked against the
+    recording test launcher in tests/; with sanitize, built with ASan and
+    UBSan into HOST_LIB_SAN."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in CPP_SOURCES]
     srcs.append(os.path.join(ROOT, "tests", "fake_launch.cpp"))
-    tmp = HOST_LIB + ".tmp"
-    _run(["g++", *CXX_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-shared", "-o", tmp, *srcs],
-         verbose)
-    os.replace(tmp, HOST_LIB)
-    return HOST_LIB
+    out = HOST_LIB_SAN if sanitize else HOST_LIB
+    tmp = out + ".tmp"
+    flags = CXX_FLAGS + (SAN_FLAGS if sanitize else [])
+    _run(["g++", *flags, f"-I{INCLUDE}", f"-I{CSRC}", "-shared", "-o", tmp, *srcs], verbose)
+    os.replace(tmp, out)
+    return out
 
 
-def host_lib_stale() -> bool:
-    if not os.path.exists(HOST_LIB):
+def asan_runtime() -> str:
+    """Path of the ASan runtime g++ links against (for LD_PRELOAD)."""
+    r = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True, text=True)
+    return os.path.realpath(r.stdout.strip())
+
+
+def host_lib_stale(path: str = HOST_LIB) -> bool:
+    if not os.path.exists(path):
         return True
-    t = os.path.getmtime(HOST_LIB)
+    t = os.path.getmtime(path)
     deps = [os.path.join(CSRC, s) for s in os.listdir(CSRC)]
-    deps += [os.path.join(INCLUDE, "kvc.h"), os.path.join(ROOT, "tests", "fake_launch.cpp")]
+    deps += [os.path.join(INCLUDE, "kvc.h"), os.path.join(ROOT, "tests", "fake_launch.cpp"),
+             os.path.join(ROOT, "tests", "e4m3_rule.hpp"), os.path.abspath(__file__)]
     return any(os.path.getmtime(p) > t for p in deps if os.path.exists(p))
 
 

@@ -32,7 +32,7 @@ constexpr int kMaxWg = kAttnMaxWg;      // persistent workgroups at most (2 per 
 constexpr int kMinPieceKeys = 1024;    // smallest share of a row worth splitting off
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kMl = 3 * 32;             // per wave: (reference, sum, exact sum) per query
+constexpr int kMl = 2 * 32;             // per wave: (reference, sum) per query
 static_assert(kWaves * kQW == kBq, "row = waves x queries per wave");
 
 struct SegArg {
@@ -53,9 +53,11 @@ struct AttnArgs {
   const int* qrows;         // active-row calls: query i is row qrows[i] of q / o / lse
   const int* qcount;        // active-row calls: number of active rows (device memory)
   const float* qrope;       // optional rotation of q rows: [ld][D/2][(cos, sin)]
-  float* part_o;            // [2*nwg][kBq*D] partial O, accumulator layout
-  float* part_ml;           // [2*nwg][waves][3][32] partial reference, sum, exact sum
-  unsigned* counters;       // [nrows][2]: arrived, partials written
+  float* part_o;            // [2*kMaxWg][kBq*D] partial O, accumulator layout
+  float* part_ml;           // [2*kMaxWg][waves][2][32] partial reference and sum
+  unsigned long long* arrive;   // [nrows]: (epoch << 32) | pieces of the row arrived
+  unsigned* tags;           // [2*kMaxWg]: epoch of the call that stored each partial
+  unsigned epoch;           // this call's epoch (nonzero)
   int n;                    // queries of the call (active-row calls: at most)
   int ld;                   // rows of q / o; row stride of lse
   int heads;
@@ -318,17 +320,32 @@ __device__ __forceinline__ void vote2(int (&slot)[kWaves][2], int wave, int lane
 
 // End of a row piece.  oacc holds this wave's unnormalised O^T (accumulator
 // layout: register i of block db is feature db*32 + (i/4)*8 + (lane/32)*4 +
-// i%4 of query qbase + lane%32), m_run the reference (log2 units), l_tot the
-// row sum that normalises O, le_tot the sum for the lse output.  A piece that
-// covers its whole row writes O / l (bf16) and lse; otherwise it stores its
-// partial, and the last piece of the row to arrive merges all partials in
-// piece order.  `s_ticket` is a workgroup-shared word.
+// i%4 of query qbase + lane%32), m_run the reference (log2 units) and l_tot
+// the row sum that normalises O (the lse output is m_run + log2 l_tot, in
+// natural-log units).  A piece that covers its whole row writes O / l (bf16)
+// and lse; otherwise the last piece of the row to arrive merges every
+// piece's partial in piece order, and the others store theirs.
+//
+// Protocol (every word tagged with the call's epoch, so nothing is reset and
+// stale words from earlier calls are told apart):
+//   - arrival: one 64-bit compare-and-swap on the row's word, which holds
+//     (epoch << 32) | pieces arrived; a word of another epoch counts as zero.
+//     The piece that makes the count npieces merges.
+//   - a storing piece writes its partial with agent-scope atomic stores,
+//     every wave waits for their completion, and then the tag of its slot is
+//     set to the epoch with release ordering at agent scope.
+//   - the merging piece waits until every other piece's tag holds the epoch
+//     (relaxed loads, bounded), takes an agent-scope acquire fence, and reads
+//     the partials with agent-scope atomic loads.  Should the bound ever be
+//     reached, the row is written as NaN rather than silently missing a
+//     partial; a late store can only set a tag to this epoch, which no later
+//     call takes for its own.
+// `s_ticket` is a workgroup-shared word.
 template <int D, bool kLse>
 __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)[D / 32],
-                                             float m_run, float l_tot, float le_tot, int r,
-                                             int h, int qbase, bool first_piece, int w,
-                                             int wave, int lane, unsigned& s_ticket,
-                                             const Split& sp) {
+                                             float m_run, float l_tot, int r, int h, int qbase,
+                                             bool first_piece, int w, int wave, int lane,
+                                             unsigned& s_ticket, const Split& sp) {
   constexpr int kDB = D / 32;
   const int tid = threadIdx.x;
   const int col = lane & 31;
@@ -338,60 +355,66 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
   const int w_hi = owner_of(rs + a.ntiles - 1, sp);
   if (w_hi > w_lo) {
     // this row is split: the last piece to arrive merges the others
-    unsigned* arrived = a.counters + 2 * r;
-    unsigned* written = arrived + 1;
     const unsigned npieces = static_cast<unsigned>(w_hi - w_lo + 1);
     __syncthreads();
-    if (tid == 0)
-      s_ticket = __hip_atomic_fetch_add(arrived, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      unsigned long long* word = a.arrive + r;
+      const unsigned long long mine = static_cast<unsigned long long>(a.epoch) << 32;
+      unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned long long next;
+      do {
+        next = (old >> 32) == a.epoch ? old + 1 : mine | 1u;
+      } while (!__hip_atomic_compare_exchange_strong(word, &old, next, __ATOMIC_RELAXED,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      s_ticket = static_cast<unsigned>(next);
+    }
     __syncthreads();
-    const bool last = s_ticket == npieces - 1;
-    const int slot = first_piece ? 0 : 1;
+    const bool last = s_ticket == npieces;
     const size_t o_wave = static_cast<size_t>(wave) * kQW * D;
     const size_t ml_wave = static_cast<size_t>(wave) * kMl;
     if (!last) {
-      // Partials are written and read with device-scope relaxed atomics
-      // (write-through, coherent across the XCDs' L2s), ordered by waiting
-      // for completion before the counter update: no cache writeback needed.
-      float* po = a.part_o + static_cast<size_t>(2 * w + slot) * kBq * D + o_wave;
+      const int slot = 2 * w + (first_piece ? 0 : 1);
+      float* po = a.part_o + static_cast<size_t>(slot) * kBq * D + o_wave;
 #pragma unroll
       for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           __hip_atomic_store(po + (db * 16 + i) * 64 + lane, oacc[db][i], __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
-      float* pml = a.part_ml + static_cast<size_t>(2 * w + slot) * kWaves * kMl + ml_wave;
+      float* pml = a.part_ml + static_cast<size_t>(slot) * kWaves * kMl + ml_wave;
       if (half == 0) {
         __hip_atomic_store(pml + 0 * 32 + col, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(pml + 1 * 32 + col, l_tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(pml + 2 * 32 + col, le_tot, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
       }
       __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): stores complete
       __syncthreads();
       if (tid == 0)
-        __hip_atomic_fetch_add(written, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.tags + slot, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
     // wait until every other piece has stored its partial (they have all
     // arrived already, so this is a short wait), then merge in piece order
     // whoever merges, so the result is bitwise the same from run to run:
-    // sum_i O_i 2^(m_i - m_max), starting from the first piece
-    // The wait is bounded: the pieces waited for have all arrived and only
-    // have their stores left.  Should the bound ever be reached, the merged
-    // row is NaN rather than silently missing a partial.  (The flag has a
-    // word of its own: other waves may still be reading s_ticket.)
+    // sum_i O_i 2^(m_i - m_max), starting from the first piece.  (The flag
+    // has a word of its own: other waves may still be reading s_ticket.)
     __shared__ unsigned s_missing;
     if (tid == 0) {
-      unsigned missing = 1;
-      for (int spin = 0; spin < (1 << 26); ++spin) {
-        if (__hip_atomic_load(written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
-            npieces - 1) {
-          missing = 0;
-          break;
+      unsigned missing = 0;
+      int budget = 1 << 26;
+      for (int ow = w_lo; ow <= w_hi; ++ow) {
+        if (ow == w) continue;
+        const int oslot = 2 * ow + (range_begin(ow, sp) >= rs ? 0 : 1);
+        while (__hip_atomic_load(a.tags + oslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+               a.epoch) {
+          if (--budget <= 0) {
+            missing = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        __builtin_amdgcn_s_sleep(1);
+        if (missing) break;
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       s_missing = missing;
     }
     __syncthreads();
@@ -399,27 +422,25 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
     float mmax = m_run;
     for (int ow = w_lo; ow <= w_hi; ++ow) {
       if (ow == w) continue;
-      const int oslot = range_begin(ow, sp) >= rs ? 0 : 1;
-      const float* pml = a.part_ml + static_cast<size_t>(2 * ow + oslot) * kWaves * kMl + ml_wave;
+      const int oslot = 2 * ow + (range_begin(ow, sp) >= rs ? 0 : 1);
+      const float* pml = a.part_ml + static_cast<size_t>(oslot) * kWaves * kMl + ml_wave;
       mmax = fmaxf(mmax, __hip_atomic_load(pml + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     }
     f32x16_t acc[kDB];
-    float l_acc = 0.f, le_acc = 0.f;
+    float l_acc = 0.f;
     for (int ow = w_lo; ow <= w_hi; ++ow) {
       const bool first = ow == w_lo;
-      float mo = m_run, lo = l_tot, leo = le_tot;
+      float mo = m_run, lo = l_tot;
       f32x16_t v[kDB];
       if (ow == w) {
 #pragma unroll
         for (int db = 0; db < kDB; ++db) v[db] = oacc[db];
       } else {
-        const int oslot = range_begin(ow, sp) >= rs ? 0 : 1;
-        const float* po = a.part_o + static_cast<size_t>(2 * ow + oslot) * kBq * D + o_wave;
-        const float* pml =
-            a.part_ml + static_cast<size_t>(2 * ow + oslot) * kWaves * kMl + ml_wave;
+        const int oslot = 2 * ow + (range_begin(ow, sp) >= rs ? 0 : 1);
+        const float* po = a.part_o + static_cast<size_t>(oslot) * kBq * D + o_wave;
+        const float* pml = a.part_ml + static_cast<size_t>(oslot) * kWaves * kMl + ml_wave;
         mo = __hip_atomic_load(pml + 0 * 32 + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         lo = __hip_atomic_load(pml + 1 * 32 + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        leo = __hip_atomic_load(pml + 2 * 32 + col, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
         for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -433,17 +454,11 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] = first ? v[db][i] * f : fmaf(v[db][i], f, acc[db][i]);
       l_acc = first ? lo * f : fmaf(lo, f, l_acc);
-      le_acc = first ? leo * f : fmaf(leo, f, le_acc);
     }
 #pragma unroll
     for (int db = 0; db < kDB; ++db) oacc[db] = acc[db];
     m_run = mmax;
     l_tot = poisoned ? __builtin_nanf("") : l_acc;
-    le_tot = poisoned ? __builtin_nanf("") : le_acc;
-    if (tid == 0) {
-      __hip_atomic_store(arrived, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(written, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 
   const int g = query_row(a, sp, qbase + col);
@@ -465,15 +480,14 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
       *reinterpret_cast<uint2*>(orow + db * 32 + g * 8 + half * 4) = make_uint2(wv[0], wv[1]);
     }
   if (kLse && half == 0)
-    a.lse[static_cast<size_t>(h) * a.ld + g] = (m_run + __log2f(le_tot)) * kLn2;
+    a.lse[static_cast<size_t>(h) * a.ld + g] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
 // Host side: kernel arguments from a launch description (segment table in
-// steps of step_keys keys, rows, grid, workspace).  Returns KVC_OK or
-// KVC_E_INVAL.
-kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a);
-// zero `n` words on the stream (a kernel, not a memset: capturable)
-void launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t stream);
+// steps of step_keys keys, rows, grid, workspace); before a ring's first call
+// (workspace not ready) it also zeroes the workspace's arrival words and tags
+// on the stream.  Returns KVC_OK or KVC_E_INVAL.
+kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a, hipStream_t stream);
 
 // the fp8 launcher (attn_fwd_fp8.hip)
 kvc_status launch_fp8(const AttnDesc& d, hipStream_t stream);

@@ -406,8 +406,8 @@ void attn_fwd_bf16(const AttnArgs a) {
     // the log-sum-exp output is that of the weights applied: reference +
     // log of the same sum O is divided by (within ln(1 + 2^-8) of the sum
     // of the unrounded p, each weight being rounded to bf16 once)
-    finish_piece<D, kLse>(a, oacc, m_ref, l_tot, l_tot, r, h, qbase, first_piece, w, wave,
-                          lane, s_ticket, sp);
+    finish_piece<D, kLse>(a, oacc, m_ref, l_tot, r, h, qbase, first_piece, w, wave, lane,
+                          s_ticket, sp);
   };
 
   // The pieces of this workgroup's range (one per row it touches).
@@ -441,9 +441,8 @@ void attn_fwd_bf16(const AttnArgs a) {
 template <int D>
 kvc_status launch_bf16(const AttnDesc& d, hipStream_t stream) {
   AttnArgs a;
-  const kvc_status st = fill_args(d, Geo<D>::kStep, a);
+  const kvc_status st = fill_args(d, Geo<D>::kStep, a, stream);
   if (st != KVC_OK) return st;
-  if (!d.workspace_ready) launch_fill_u32(a.counters, 2 * a.nrows, 0u, stream);
   const dim3 grid(a.nwg), block(kThreads);
   // active-row calls have instances of their own (their split is taken in
   // the kernel); whole rows first only on the plain call over long rows
@@ -489,11 +488,7 @@ int device_cus() {
 
 }  // namespace
 
-void launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t stream) {
-  hipLaunchKernelGGL(fill_u32, dim3((n + 255) / 256), dim3(256), 0, stream, p, n, v);
-}
-
-kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a) {
+kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a, hipStream_t stream) {
   a.q = static_cast<const uint16_t*>(d.q);
   a.o = static_cast<uint16_t*>(d.o);
   a.lse = d.lse;
@@ -527,15 +522,20 @@ kvc_status fill_args(const AttnDesc& d, int step_keys, AttnArgs& a) {
   const long long slots = std::min(2 * device_cus(), kMaxWg);
   const long long by_size = std::max<long long>(1, a.total * step_keys / kMinPieceKeys);
   a.nwg = static_cast<int>(std::min(slots, by_size));
-  // workspace: counters, then partial reference/sums, then partial O
+  // workspace: arrival words, partial tags, partial reference/sums, partial O
+  const WorkLayout L = attention_workspace_layout(d.heads, d.head_dim, d.n);
+  static_assert(sizeof(float) * kWaves * kMl == sizeof(float) * 2 * kAttnRowQueries,
+                "partial reference/sum slot size");
+  if (L.rows < a.nrows || d.workspace_bytes < L.total || d.epoch == 0) return KVC_E_INVAL;
   unsigned char* ws = static_cast<unsigned char*>(d.workspace);
-  const size_t cnt_bytes = align_up(sizeof(unsigned) * 2 * a.nrows, 256);
-  const size_t ml_bytes = align_up(sizeof(float) * 2 * kMaxWg * kWaves * kMl, 256);
-  const size_t po_bytes = sizeof(float) * 2 * kMaxWg * kBq * d.head_dim;
-  if (d.workspace_bytes < cnt_bytes + ml_bytes + po_bytes) return KVC_E_INVAL;
-  a.counters = reinterpret_cast<unsigned*>(ws);
-  a.part_ml = reinterpret_cast<float*>(ws + cnt_bytes);
-  a.part_o = reinterpret_cast<float*>(ws + cnt_bytes + ml_bytes);
+  a.arrive = reinterpret_cast<unsigned long long*>(ws + L.arrive_off);
+  a.tags = reinterpret_cast<unsigned*>(ws + L.tags_off);
+  a.part_ml = reinterpret_cast<float*>(ws + L.ml_off);
+  a.part_o = reinterpret_cast<float*>(ws + L.po_off);
+  a.epoch = d.epoch;
+  if (!d.workspace_ready)
+    hipLaunchKernelGGL(fill_u32, dim3((L.zero_words + 255) / 256), dim3(256), 0, stream,
+                       reinterpret_cast<unsigned*>(ws), L.zero_words, 0u);
   return KVC_OK;
 }
 

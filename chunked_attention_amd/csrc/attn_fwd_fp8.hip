@@ -426,7 +426,7 @@ void attn_fwd_fp8(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[db][i] *= vs_cur;
     const float l_tot = lacc[0];
-    finish_piece<D, kLse>(a, oacc, m_ref, l_tot, l_tot, r, h, qbase, first_piece, w, wave, lane,
+    finish_piece<D, kLse>(a, oacc, m_ref, l_tot, r, h, qbase, first_piece, w, wave, lane,
                           s_ticket, sp);
   };
 
@@ -461,11 +461,10 @@ void attn_fwd_fp8(const AttnArgs a) {
 template <int D>
 kvc_status launch_fp8_d(const AttnDesc& d, hipStream_t stream) {
   AttnArgs a;
-  const kvc_status st = fill_args(d, kBk, a);
+  for (int s = 0; s < d.nseg; ++s)
+    if (!d.seg[s].k_scale || !d.seg[s].v_scale) return KVC_E_INVAL;
+  const kvc_status st = fill_args(d, kBk, a, stream);
   if (st != KVC_OK) return st;
-  for (int s = 0; s < a.nseg; ++s)
-    if (!a.seg[s].ks || !a.seg[s].vs) return KVC_E_INVAL;
-  if (!d.workspace_ready) launch_fill_u32(a.counters, 2 * a.nrows, 0u, stream);
   const dim3 grid(a.nwg), block(kThreads);
   // whole rows first only on the plain call over long rows (RoPE and
   // active-row calls keep one instance each)

@@ -100,9 +100,9 @@ __global__ __launch_bounds__(kThreads) void cache_write_bf16(
 // ----------------------------------------------------------------- fp8 ----
 
 // E4M3 codes of two float32 values (byte 0: a, byte 1: b): nearest, ties to
-// even, saturating at +-448, NaN -> 0x7F with the sign kept (the rule
-// written out in e4m3.hpp), taken by the hardware conversion (nearest-even on
-// finite values up to 448) after an explicit saturation.
+// even, saturating at +-448, NaN -> 0x7F with the sign kept, taken by the
+// hardware conversion (nearest-even on finite values up to 448) after an
+// explicit saturation.
 __device__ __forceinline__ uint32_t e4m3x2(float a, float b) {
   const float ca = fminf(fmaxf(a, -448.0f), 448.0f);
   const float cb = fminf(fmaxf(b, -448.0f), 448.0f);

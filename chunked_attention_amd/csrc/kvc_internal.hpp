@@ -79,7 +79,8 @@ struct AttnDesc {
   AttnSegment seg[kMaxSegments];
   void* workspace = nullptr;    // device scratch for split partials
   size_t workspace_bytes = 0;
-  bool workspace_ready = false; // counters in the workspace already zeroed
+  bool workspace_ready = false; // arrival words and tags in the workspace already zeroed
+  uint32_t epoch = 1;           // nonzero, different from the previous call's on this workspace
 };
 
 // LiveEdit active-row mask (validated by the caller).
@@ -100,7 +101,21 @@ kvc_status launch_cache_write(const CacheWriteDesc& d, void* stream);
 kvc_status launch_attention(const AttnDesc& d, void* stream);
 kvc_status launch_edit_mask(const EditMaskDesc& d, void* stream);
 
-// Workspace bytes the attention launcher may use for a ring of this shape.
+// Attention workspace of a ring whose calls have n queries (byte offsets
+// from its start, each part 256-byte aligned):
+//   arrive  uint64 [rows]: per 128-query row, (epoch << 32) | pieces arrived
+//   tags    uint32 [2 * kAttnMaxWg]: per partial slot, the epoch of the call
+//           that last stored it
+//   ml      float32 [2 * kAttnMaxWg][4 waves][2][32]: partial reference and sum
+//   po      float32 [2 * kAttnMaxWg][kAttnRowQueries * head_dim]: partial O
+// The arrival words and tags are zero before a ring's first call; after that
+// the epoch of each call tells its own words from stale ones.
+struct WorkLayout {
+  size_t arrive_off = 0, tags_off = 0, ml_off = 0, po_off = 0, total = 0;
+  int rows = 0;            // 128-query rows
+  int zero_words = 0;      // 32-bit words from the start to zero before first use
+};
+WorkLayout attention_workspace_layout(int heads, int head_dim, int n);
 size_t attention_workspace_bytes(int heads, int head_dim, int n, int kv_dtype);
 
 }  // namespace kvc

@@ -4,20 +4,22 @@
 
 namespace kvc {
 
-// Workspace of the attention kernel: per row two counters (pieces arrived,
-// partials written), then per persistent workgroup two partial slots, each
-// holding the reference max and two sums (of the bf16-rounded and of the
-// exact probabilities) of its queries and the unnormalised fp32 output
-// [kAttnRowQueries][d].
+WorkLayout attention_workspace_layout(int heads, int head_dim, int n) {
+  WorkLayout L;
+  L.rows = heads * ((n + kAttnRowQueries - 1) / kAttnRowQueries);
+  const size_t slots = 2 * static_cast<size_t>(kAttnMaxWg);
+  L.arrive_off = 0;
+  L.tags_off = align_up(sizeof(unsigned long long) * L.rows, 256);
+  L.ml_off = L.tags_off + align_up(sizeof(unsigned) * slots, 256);
+  L.po_off = L.ml_off + align_up(sizeof(float) * slots * 2 * kAttnRowQueries, 256);
+  L.total = L.po_off + sizeof(float) * slots * kAttnRowQueries * static_cast<size_t>(head_dim);
+  L.zero_words = static_cast<int>(L.ml_off / sizeof(unsigned));
+  return L;
+}
+
 size_t attention_workspace_bytes(int heads, int head_dim, int n, int kv_dtype) {
   (void)kv_dtype;
-  const size_t nrows = static_cast<size_t>(heads) *
-                       ((n + kAttnRowQueries - 1) / kAttnRowQueries);
-  const size_t counters = align_up(sizeof(unsigned) * 2 * nrows, 256);
-  const size_t ml = align_up(sizeof(float) * 2 * kAttnMaxWg * 3 * kAttnRowQueries, 256);
-  const size_t po = sizeof(float) * 2 * static_cast<size_t>(kAttnMaxWg) * kAttnRowQueries *
-                    head_dim;
-  return counters + ml + po;
+  return attention_workspace_layout(heads, head_dim, n).total;
 }
 
 }  // namespace kvc

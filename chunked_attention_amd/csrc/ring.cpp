@@ -122,7 +122,8 @@ struct kvc_ring {
   int current;            // slot of the current chunk (STAGED or COMMITTED)
   int cond_valid;
   int ref_valid;
-  int work_ready;         // attention workspace counters initialised
+  int work_ready;         // attention workspace arrival words and tags zeroed
+  uint32_t epoch;         // epoch of the last attention call (0: none yet)
 };
 
 namespace kvc {
@@ -242,8 +243,14 @@ kvc_status attention_call(kvc_ring* r, const void* q, void* o, float* lse, const
   d.workspace = r->base + r->L.work_off;
   d.workspace_bytes = r->L.work_bytes;
   d.workspace_ready = r->work_ready != 0;
+  // every call gets a new nonzero epoch: the kernel tells this call's
+  // arrival words and partial tags in the workspace from earlier calls' by it
+  d.epoch = r->epoch + 1 == 0 ? 1 : r->epoch + 1;
   kvc_status s = launch_attention(d, stream);
-  if (s == KVC_OK) r->work_ready = 1;
+  if (s == KVC_OK) {
+    r->work_ready = 1;
+    r->epoch = d.epoch;
+  }
   return s;
 }
 

@@ -9,7 +9,7 @@
 #include <cstring>
 #include <vector>
 
-#include "e4m3.hpp"
+#include "e4m3_rule.hpp"
 #include "kvc_internal.hpp"
 
 namespace {
@@ -36,6 +36,8 @@ struct Record {
   uint64_t qrows;     // attention: active-row map (0: all rows)
   uint64_t qcount;    // attention: active-row count
   uint64_t rope;      // write: K rotation table; attention: q rotation table
+  uint32_t epoch;     // attention: the call's epoch
+  int32_t ws_ready;   // attention: workspace already zeroed by an earlier call
 };
 
 std::vector<Record> g_log;
@@ -90,6 +92,8 @@ kvc_status launch_attention(const AttnDesc& d, void* stream) {
   r.qrows = reinterpret_cast<uint64_t>(d.qrows);
   r.qcount = reinterpret_cast<uint64_t>(d.qcount);
   r.rope = reinterpret_cast<uint64_t>(d.qrope);
+  r.epoch = d.epoch;
+  r.ws_ready = d.workspace_ready ? 1 : 0;
   g_log.push_back(r);
   return KVC_OK;
 }
@@ -126,7 +130,8 @@ int32_t kvcfake_get(int32_t i, void* out) {
   return 0;
 }
 
-// The product's E4M3 encoder, exposed for CPU tests against the oracle.
+// The C statement of the E4M3 rule (e4m3_rule.hpp), for CPU tests against
+// the oracle.
 void kvcfake_e4m3_encode(const float* x, uint8_t* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = kvc::e4m3_from_float(x[i]);
 }

@@ -47,7 +47,7 @@ def test_library_has_gfx950_code_object():
 def test_host_only_calls_without_device(lib):
     cfg = kv.make_config(40, 128, 1620, 256, 3)
     need = lib.kvc_required_bytes(ctypes.byref(cfg))
-    assert need == 2 * 40 * 128 * 2 * (256 + 5 * 1664) + 4352 + 1572864 + 67108864
+    assert need == 2 * 40 * 128 * 2 * (256 + 5 * 1664) + 4352 + 4096 + 1048576 + 67108864
     h = ctypes.c_void_p()
     base = 0x7F0000000000
     assert lib.kvc_create(ctypes.byref(cfg), ctypes.c_void_p(base), need,

@@ -6,6 +6,7 @@ device buffer is a fake, aligned address that the host code never
 dereferences.
 """
 import ctypes
+import os
 import math
 
 import numpy as np
@@ -29,14 +30,20 @@ class Record(ctypes.Structure):
                 ("scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
                 ("k_scale", ctypes.c_uint64), ("stream", ctypes.c_uint64),
                 ("qrows", ctypes.c_uint64), ("qcount", ctypes.c_uint64),
-                ("rope", ctypes.c_uint64)]
+                ("rope", ctypes.c_uint64), ("epoch", ctypes.c_uint32),
+                ("ws_ready", ctypes.c_int32)]
 
 
 @pytest.fixture(scope="module")
 def lib():
-    if kbuild.host_lib_stale():
-        kbuild.build_host()
-    L = kv.declare(ctypes.CDLL(kbuild.HOST_LIB))
+    # KVC_HOST_SANITIZE=1: the AddressSanitizer + UBSan build of the same
+    # sources (run by test_host_sanitizers.py in a process that preloads the
+    # sanitizer runtime)
+    sanitize = os.environ.get("KVC_HOST_SANITIZE") == "1"
+    path = kbuild.HOST_LIB_SAN if sanitize else kbuild.HOST_LIB
+    if kbuild.host_lib_stale(path):
+        kbuild.build_host(sanitize=sanitize)
+    L = kv.declare(ctypes.CDLL(path))
     L.kvcfake_record_size.restype = ctypes.c_int32
     L.kvcfake_count.restype = ctypes.c_int32
     L.kvcfake_get.argtypes = [ctypes.c_int32, ctypes.c_void_p]
@@ -114,11 +121,13 @@ def expected_bytes(H, d, n, m, W, e, fp8, r=0, s=0):
         (slot(s) if s else 0)
     if fp8:
         total += al(4 * 2 * H * (P(max(n, m, r, s)) // 64))
-    # attention workspace: 2 counters per 128-query row (n + s queries), then 2
-    # partial slots per persistent workgroup (512 at most): max + 2 sums and
+    # attention workspace: one 64-bit arrival word per 128-query row (n + s
+    # queries), one 32-bit tag per partial slot (2 per persistent workgroup,
+    # 512 at most), then per slot the reference and sum of 128 queries and the
     # fp32 O [128][d]
     rows = H * ((n + s + 127) // 128)
-    total += al(8 * rows) + al(4 * 2 * 512 * 3 * 128) + 4 * 2 * 512 * 128 * d
+    total += al(8 * rows) + al(4 * 2 * 512) + al(4 * 2 * 512 * 2 * 128) + \
+        4 * 2 * 512 * 128 * d
     return total
 
 
@@ -136,7 +145,7 @@ def test_720p_ring_size():
     # 720p bf16: cond 256 rows + 5 slots of 1620 rows (padded to 1664), 40
     # heads, plus the attention workspace (520 rows; 512 workgroups x 2 slots)
     assert expected_bytes(40, 128, 1620, 256, 3, 2, False) == \
-        2 * 40 * 128 * 2 * (256 + 5 * 1664) + 4352 + 1572864 + 67108864
+        2 * 40 * 128 * 2 * (256 + 5 * 1664) + 4352 + 4096 + 1048576 + 67108864
 
 
 @pytest.mark.parametrize("bad", [
@@ -370,7 +379,30 @@ def test_fp8_ring_records_scales(lib):
     r.close()
 
 
-def test_product_e4m3_encoder_matches_oracle(lib):
+def test_attention_epochs(lib):
+    # Every attention call gets a new nonzero epoch (the kernel tells its own
+    # arrival words and partial tags in the workspace from stale ones by it);
+    # only the first call asks for the workspace to be zeroed; a failed call
+    # consumes no epoch.
+    r = FakeRing(lib, W=1)
+    assert r.append(kv.KVC_COND) == kv.KVC_OK
+    assert r.append(kv.KVC_STAGE) == kv.KVC_OK
+    epochs = []
+    for i in range(3):
+        assert r.attn() == kv.KVC_OK
+        rec = r.last()
+        assert rec.kind == 1
+        epochs.append(rec.epoch)
+        assert rec.ws_ready == (0 if i == 0 else 1)
+    assert epochs == [1, 2, 3]
+    lib.kvcfake_fail_next(kv.KVC_E_DEVICE)
+    assert r.attn() == kv.KVC_E_DEVICE
+    assert r.attn() == kv.KVC_OK
+    assert r.last().epoch == 4
+    r.close()
+
+
+def test_c_e4m3_rule_matches_oracle(lib):
     rng = np.random.default_rng(0)
     pos = O3.decode_table()[:127]
     mids = (pos[1:] + pos[:-1]) / 2
