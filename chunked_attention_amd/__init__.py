@@ -25,6 +25,9 @@ KVC_E_STATE = -2
 KVC_E_NOMEM = -3
 KVC_E_DEVICE = -4
 KVC_E_UNSUPPORTED = -5
+KVC_E_SCRATCH = -6
+KVC_NOALLOC_MAX_ROWS = 8192
+KVC_NOALLOC_SCRATCH_BYTES = 65536 + 4096 + 1048576 + 67108864
 
 KVC_KV_BF16 = 0
 KVC_KV_FP8_E4M3 = 1
@@ -74,6 +77,7 @@ EXPORTS = (
     "kvc_required_bytes", "kvc_create", "kvc_append_chunk", "chunk_attn_fwd", "kvc_evict",
     "kvc_destroy", "kvc_status_str", "kvc_get_info", "kvc_get_segments", "kvc_get_slot",
     "chunk_attn_fwd_rows", "kvc_edit_mask", "kvc_append_chunk_rope", "chunk_attn_fwd_rope",
+    "chunk_attn_fwd_noalloc",
 )
 
 
@@ -90,6 +94,8 @@ def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.kvc_append_chunk.restype = I
     lib.chunk_attn_fwd.argtypes = [P, P, P, P, P]
     lib.chunk_attn_fwd.restype = I
+    lib.chunk_attn_fwd_noalloc.argtypes = [P, P, P, P, P]
+    lib.chunk_attn_fwd_noalloc.restype = I
     lib.chunk_attn_fwd_rows.argtypes = [P, P, P, P, P, P, P]
     lib.chunk_attn_fwd_rows.restype = I
     lib.kvc_edit_mask.argtypes = [P, P, I, I, ctypes.c_float, I, P, P, P]
@@ -243,6 +249,13 @@ def _check_i32(x, what: str, numel: int | None = None) -> None:
 def chunk_attn_fwd(handle, cfg: kvc_config, q, o, lse=None, stream=None) -> None:
     _check(lib().chunk_attn_fwd(handle, *_attn_args(cfg, q, o, lse), _stream_handle(stream)),
            "chunk_attn_fwd")
+
+
+def chunk_attn_fwd_noalloc(handle, cfg: kvc_config, q, o, lse=None, stream=None) -> None:
+    """chunk_attn_fwd with the split-row scratch in the library's static
+    device array (no allocation; calls on one device must not overlap)."""
+    _check(lib().chunk_attn_fwd_noalloc(handle, *_attn_args(cfg, q, o, lse),
+                                        _stream_handle(stream)), "chunk_attn_fwd_noalloc")
 
 
 def chunk_attn_fwd_rows(handle, cfg: kvc_config, q, o, rows, count, lse=None,

@@ -31,7 +31,8 @@ HOST_LIB_SAN = os.path.join(BUILD, "libkvc_hostcheck_san.so")
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
              "-fno-omit-frame-pointer", "-g"]
 
-HIP_SOURCES = ["cache_write.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "edit_mask.hip"]
+HIP_SOURCES = ["cache_write.hip", "attn_fwd.hip", "attn_fwd_fp8.hip", "edit_mask.hip",
+               "noalloc.hip"]
 CPP_SOURCES = ["ring.cpp", "plan.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -118,4 +118,20 @@ struct WorkLayout {
 WorkLayout attention_workspace_layout(int heads, int head_dim, int n);
 size_t attention_workspace_bytes(int heads, int head_dim, int n, int kv_dtype);
 
+// The attention workspace held in the library's static device array
+// (chunk_attn_fwd_noalloc), on the current device.
+struct StaticWork {
+  void* ptr = nullptr;      // device address of the array on this device
+  size_t bytes = 0;
+  bool ready = false;       // arrival words and tags already zeroed on this device
+  uint32_t epoch = 0;       // this call's epoch on this device (nonzero)
+  int device = -1;
+};
+// Fills `w` for a call needing `need` bytes: KVC_E_SCRATCH if need exceeds
+// KVC_NOALLOC_SCRATCH_BYTES, KVC_E_DEVICE if the runtime fails.  Allocates
+// nothing.
+kvc_status static_workspace(size_t need, StaticWork& w);
+// after a successful launch with `w`: its zeroing has been enqueued
+void static_workspace_launched(const StaticWork& w);
+
 }  // namespace kvc

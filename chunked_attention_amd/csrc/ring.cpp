@@ -222,7 +222,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 kvc_status attention_call(kvc_ring* r, const void* q, void* o, float* lse, const float* rope,
-                          const int32_t* rows, const int32_t* count, void* stream) {
+                          const int32_t* rows, const int32_t* count, void* stream,
+                          bool static_work = false) {
   if (!r || !q || !o || !aligned16(q) || !aligned16(o) || q == o) return KVC_E_INVAL;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return KVC_E_INVAL;
   if (rope && !aligned16(rope)) return KVC_E_INVAL;
@@ -240,6 +241,21 @@ kvc_status attention_call(kvc_ring* r, const void* q, void* o, float* lse, const
   d.head_dim = r->cfg.head_dim;
   d.kv_dtype = r->cfg.kv_dtype;
   d.scale = r->scale;
+  if (static_work) {
+    // the library's static device array on the current device (its own
+    // epochs: it is shared by every ring on the device)
+    StaticWork sw;
+    const kvc_status ws = static_workspace(
+        attention_workspace_bytes(d.heads, d.head_dim, d.n, d.kv_dtype), sw);
+    if (ws != KVC_OK) return ws;
+    d.workspace = sw.ptr;
+    d.workspace_bytes = sw.bytes;
+    d.workspace_ready = sw.ready;
+    d.epoch = sw.epoch;
+    const kvc_status s = launch_attention(d, stream);
+    if (s == KVC_OK) static_workspace_launched(sw);
+    return s;
+  }
   d.workspace = r->base + r->L.work_off;
   d.workspace_bytes = r->L.work_bytes;
   d.workspace_ready = r->work_ready != 0;
@@ -351,6 +367,11 @@ kvc_status chunk_attn_fwd(kvc_ring* r, const void* q, void* o, float* lse, void*
   return attention_call(r, q, o, lse, nullptr, nullptr, nullptr, stream);
 }
 
+kvc_status chunk_attn_fwd_noalloc(kvc_ring* r, const void* q, void* o, float* lse,
+                                  void* stream) {
+  return attention_call(r, q, o, lse, nullptr, nullptr, nullptr, stream, true);
+}
+
 kvc_status chunk_attn_fwd_rows(kvc_ring* r, const void* q, void* o, float* lse,
                                const int32_t* rows, const int32_t* count, void* stream) {
   if (!rows || !count || !aligned4(rows) || !aligned4(count)) return KVC_E_INVAL;
@@ -431,6 +452,9 @@ const char* kvc_status_str(kvc_status s) {
     case KVC_E_NOMEM: return "KVC_E_NOMEM: buffer smaller than kvc_required_bytes";
     case KVC_E_DEVICE: return "KVC_E_DEVICE: HIP runtime error";
     case KVC_E_UNSUPPORTED: return "KVC_E_UNSUPPORTED: not supported by this library";
+    case KVC_E_SCRATCH:
+      return "KVC_E_SCRATCH: call needs more than the static scratch of chunk_attn_fwd_noalloc "
+             "(KVC_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown kvc status";
   }
 }

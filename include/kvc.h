@@ -60,6 +60,7 @@ typedef int32_t kvc_status;
 #define KVC_E_NOMEM       (-3)  /* caller buffer smaller than kvc_required_bytes */
 #define KVC_E_DEVICE      (-4)  /* the HIP runtime reported an error */
 #define KVC_E_UNSUPPORTED (-5)  /* valid request this library does not implement */
+#define KVC_E_SCRATCH     (-6)  /* chunk_attn_fwd_noalloc: needs more than its static scratch */
 
 /* K/V storage type of a ring */
 #define KVC_KV_BF16      0   /* bf16, bit copies of the caller's K/V */
@@ -189,6 +190,32 @@ kvc_status kvc_append_chunk(kvc_ring* ring, int32_t kind, const void* k, const v
  * KVC_E_DEVICE.
  */
 kvc_status chunk_attn_fwd(kvc_ring* ring, const void* q, void* o, float* lse, void* stream);
+
+/*
+ * chunk_attn_fwd without any device allocation, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, result and errors as chunk_attn_fwd (the
+ * same kernels and work split, so the output is bitwise the same); the only
+ * difference is where the kernel keeps its split-row scratch (arrival words,
+ * partial tags, partial results): in a static device array of the library,
+ * KVC_NOALLOC_SCRATCH_BYTES per device, instead of the ring's workspace.
+ *   - Each GPU the library runs on holds its own copy of the array until the
+ *     process ends; its address is taken once per device (first call with that
+ *     device current).  The call allocates and frees nothing.
+ *   - Every call on a device shares that device's array, and the array keeps
+ *     the last call's contents; only its arrival words and tags must start at
+ *     zero, which the first call on the device enqueues (a fill kernel), and
+ *     a per-device epoch tells each call's words from older ones.  Calls that
+ *     overlap on one device (on concurrent streams, or from several host
+ *     threads) race on the array: order them.
+ *   - KVC_E_SCRATCH if the call needs more scratch than the array holds
+ *     (more than KVC_NOALLOC_MAX_ROWS 128-query rows, i.e. heads *
+ *     ceil((n + s) / 128), at head_dim 128).
+ */
+#define KVC_NOALLOC_MAX_ROWS 8192
+#define KVC_NOALLOC_SCRATCH_BYTES (65536u + 4096u + 1048576u + 67108864u)
+kvc_status chunk_attn_fwd_noalloc(kvc_ring* ring, const void* q, void* o, float* lse,
+                                  void* stream);
 
 /*
  * Rotary position encoding fused into the cache write and the attention's Q

@@ -15,7 +15,7 @@
 namespace {
 
 struct Record {
-  int32_t kind;       // 0 cache write, 1 attention, 2 edit mask
+  int32_t kind;       // 0 cache write, 1 attention (dst_k: workspace), 2 edit mask
                       // (mask: rows = tokens, pitch = channels, nseg = keep,
                       // scale = tau, src_k/src_v = z_src/z_edit,
                       // dst_k/dst_vt = rows/count)
@@ -94,6 +94,7 @@ kvc_status launch_attention(const AttnDesc& d, void* stream) {
   r.rope = reinterpret_cast<uint64_t>(d.qrope);
   r.epoch = d.epoch;
   r.ws_ready = d.workspace_ready ? 1 : 0;
+  r.dst_k = reinterpret_cast<uint64_t>(d.workspace);
   g_log.push_back(r);
   return KVC_OK;
 }
@@ -115,6 +116,26 @@ kvc_status launch_edit_mask(const EditMaskDesc& d, void* stream) {
   g_log.push_back(r);
   return KVC_OK;
 }
+
+// The static workspace of chunk_attn_fwd_noalloc: a fake device address
+// (the host code never dereferences it), epochs counted as on the device.
+namespace {
+uint32_t g_static_epoch = 0;
+bool g_static_ready = false;
+}  // namespace
+
+kvc_status static_workspace(size_t need, StaticWork& w) {
+  if (need > KVC_NOALLOC_SCRATCH_BYTES) return KVC_E_SCRATCH;
+  w.ptr = reinterpret_cast<void*>(0x7E0000000000ull);
+  w.bytes = KVC_NOALLOC_SCRATCH_BYTES;
+  w.ready = g_static_ready;
+  g_static_epoch = g_static_epoch + 1 == 0 ? 1 : g_static_epoch + 1;
+  w.epoch = g_static_epoch;
+  w.device = 0;
+  return KVC_OK;
+}
+
+void static_workspace_launched(const StaticWork&) { g_static_ready = true; }
 
 }  // namespace kvc
 

@@ -402,6 +402,41 @@ def test_attention_epochs(lib):
     r.close()
 
 
+def test_noalloc_call_uses_the_static_scratch(lib):
+    # chunk_attn_fwd_noalloc: the same launch as chunk_attn_fwd but with the
+    # library's static array as workspace, epochs of its own (shared by every
+    # ring on the device), zeroing asked for only on its first use; a call
+    # needing more than the array holds is refused before any launch.
+    lib.chunk_attn_fwd_noalloc.argtypes = [ctypes.c_void_p] * 5
+    r = FakeRing(lib, W=1)
+    assert r.append(kv.KVC_COND) == kv.KVC_OK
+    assert r.append(kv.KVC_STAGE) == kv.KVC_OK
+    assert r.attn() == kv.KVC_OK
+    plain = r.last()
+    args = (r.h, ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000), None, ctypes.c_void_p(0x77))
+    epochs = []
+    for _ in range(2):
+        assert lib.chunk_attn_fwd_noalloc(*args) == kv.KVC_OK
+        rec = r.last()
+        assert rec.kind == 1 and rec.nseg == plain.nseg and rec.rows == plain.rows
+        assert rec.dst_k != plain.dst_k          # not the ring's workspace
+        epochs.append((rec.epoch, rec.ws_ready))
+    assert epochs[1][0] == epochs[0][0] + 1 and epochs[1][1] == 1
+    # the ring's own epochs are untouched
+    assert r.attn() == kv.KVC_OK and r.last().epoch == plain.epoch + 1
+    r.close()
+    # 41 heads x ceil(25600 / 128) = 8200 rows > KVC_NOALLOC_MAX_ROWS
+    big = FakeRing(lib, H=41, n=25600, m=0, W=0)
+    assert big.append(kv.KVC_STAGE) == kv.KVC_OK
+    n0 = lib.kvcfake_count()
+    st = lib.chunk_attn_fwd_noalloc(big.h, ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000),
+                                    None, None)
+    assert st == kv.KVC_E_SCRATCH
+    assert lib.kvcfake_count() == n0
+    assert b"static scratch" in lib.kvc_status_str(kv.KVC_E_SCRATCH)
+    big.close()
+
+
 def test_c_e4m3_rule_matches_oracle(lib):
     rng = np.random.default_rng(0)
     pos = O3.decode_table()[:127]
