@@ -50,56 +50,164 @@ def latent_grid(nq: int):
     return (1, nq), 1
 
 
-def cpu_baseline(w, seconds: float, seed_dist: str = "baseline") -> dict:
-    """The fp64 oracle on a bounded sample of the steady-state chunk: the
-    whole call (all heads) repeated until about `seconds` of CPU time."""
+def _oracle_call(w, seed_dist: str, fp8: bool = False, heads: int | None = None):
+    """Arguments of the oracle's call for the steady-state chunk t = W+1 (the
+    first `heads` heads, default all), in float64: bf16 inputs upcast, or for
+    fp8 rings the dequantised values the ring holds (computed by the oracle's
+    encoder; its scales are per head, so a subset of heads is exact)."""
     import numpy as np
+    import torch
     import synth
     from oracle import attention as O1
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    import torch
+    from oracle import fp8 as O3
     s = synth.Stream(w, seed_dist)
     t = w.window + 1
     ids = O1.visible_chunks(t, w.window)
-    f64 = O1.as_f64
+    hs = slice(0, heads)
+    if fp8:
+        f64 = lambda x: O3.roundtrip_segment(x[:, hs].to(torch.float32).numpy())
+    else:
+        f64 = lambda x: O1.as_f64(x[:, hs])
     ck, cv = (f64(x) for x in s.kv_cond()) if w.cond_tokens else (None, None)
     rk, rv = (f64(x) for x in s.kv_ref()) if w.ref_tokens else (None, None)
     sk, sv = (f64(x) for x in s.kv_src(t)) if w.source_tokens else (None, None)
     hist = [s.kv_clean(j) for j in ids]
     k, v = s.kv_noisy(t)
     q = torch.cat([s.q(t), s.q_src(t)]) if w.source_tokens else s.q(t)
-    args = (f64(q), ck, cv, [f64(a) for a, _ in hist], [f64(b) for _, b in hist],
-            f64(k), f64(v), w.scale)
+    args = (O1.as_f64(q[:, hs]), ck, cv, [f64(a) for a, _ in hist],
+            [f64(b) for _, b in hist], f64(k), f64(v), w.scale)
     kw = dict(ref_k=rk, ref_v=rv, src_k=sk, src_v=sv)
+    kv_len = O1.kv_length(t, w.cond_tokens, w.chunk_tokens, w.window, w.ref_tokens,
+                          w.source_tokens)
+    return t, args, kw, kv_len, np
 
+
+def _time_calls(fn, seconds: float):
+    """Runs fn until about `seconds` have passed (at least once): (calls, s)."""
     t0 = time.perf_counter()
-    O1.chunk_attention(*args, **kw)
+    fn()
     one = time.perf_counter() - t0
     reps = max(1, int(round(seconds / max(one, 1e-3))))
     t0 = time.perf_counter()
     for _ in range(reps - 1):
-        O1.chunk_attention(*args, **kw)
-    dt = one + time.perf_counter() - t0
-    kv_len = O1.kv_length(t, w.cond_tokens, w.chunk_tokens, w.window, w.ref_tokens,
-                          w.source_tokens)
-    flops = attn_flops(w, kv_len) * reps
-    return {
-        "value": flops / dt / 1e12,
+        fn()
+    return reps, one + time.perf_counter() - t0
+
+
+def cpu_baseline(w, seconds: float, seed_dist: str = "baseline", legs: bool = False) -> dict:
+    """The fp64 oracle on a bounded sample of the steady-state chunk: the
+    whole call (every head), repeated for about `seconds`.  The heads run on
+    a thread pool of one thread per core (numpy's BLAS and ufuncs release the
+    GIL; each thread calls the oracle on one head's slice, BLAS held to one
+    thread), so the host's cores all work, as in a parallel CPU run.
+
+    With `legs`, also: one core (the same call with one thread), the
+    oracle of the fp8 configuration (dequantised K/V), and the full-depth
+    configuration extrapolated from the single-layer call (48 layers x 2
+    denoise steps = 96 calls per chunk; an extrapolation, not a run)."""
+    import concurrent.futures as cf
+    from oracle import attention as O1
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    t, args, kw, kv_len, np = _oracle_call(w, seed_dist)
+    q, ck, cv, hk, hv, k, v, scale = args
+
+    def head_slice(x, h):
+        return None if x is None else x[:, h:h + 1]
+
+    def one_head(h):
+        sl = lambda x: head_slice(x, h)
+        O1.chunk_attention(sl(q), sl(ck), sl(cv), [sl(x) for x in hk], [sl(x) for x in hv],
+                           sl(k), sl(v), scale, ref_k=sl(kw["ref_k"]), ref_v=sl(kw["ref_v"]),
+                           src_k=sl(kw["src_k"]), src_v=sl(kw["src_v"]))
+
+    threads = min(cores, w.heads)
+    flops_call = attn_flops(w, kv_len)
+
+    def pooled(call_heads):
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            def run():
+                list(ex.map(call_heads, range(w.heads)))
+            if threadpool_limits is not None:
+                with threadpool_limits(limits=1):
+                    return _time_calls(run, seconds)
+            return _time_calls(run, seconds)
+
+    calls, dt = pooled(one_head)
+    out = {
+        "value": flops_call * calls / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{w.name} steady chunk t={t} ({kv_len} keys, all {w.heads} heads), "
-                  f"fp64 numpy oracle incl. explicit KV concatenation, {reps} calls in "
-                  f"{dt:.2f} s; {reps / dt:.4f} chunks/s",
+        "sample": f"{w.name} steady chunk t={t} ({kv_len} keys, all {w.heads} heads on "
+                  f"{threads} threads, one head per task), fp64 numpy oracle incl. explicit "
+                  f"KV concatenation, {calls} calls in {dt:.2f} s; {calls / dt:.4f} chunks/s",
         "seconds": dt,
-        "calls": reps,
+        "calls": calls,
+        "chunks_per_s": calls / dt,
         "cpu_model": _cpu_model(),
-        "affinity_cores": len(os.sched_getaffinity(0)),
+        "affinity_cores": cores,
     }
+    if not legs:
+        return out
+    out["legs"] = {}
+    # one core: the heads one after another, BLAS on one thread; a bounded
+    # sample of heads scaled to the whole call
+    nh = max(1, min(w.heads, int(seconds // 2) or 1))
+
+    def serial():
+        for h in range(nh):
+            one_head(h)
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            reps, ds = _time_calls(serial, seconds / 3)
+    else:
+        reps, ds = _time_calls(serial, seconds / 3)
+    call_s = ds / reps * w.heads / nh
+    out["legs"]["single_core"] = {
+        "value": flops_call / call_s / 1e12, "unit": "TFLOP/s", "cores": 1,
+        "seconds_per_call": call_s,
+        "sample": f"{nh} of {w.heads} heads, {reps} times, scaled to the whole call"}
+    # the fp8 configuration's oracle: dequantised K/V (same shape and keys)
+    import synth
+    w8 = synth.WORKLOADS["fp8"]
+    if (w8.heads, w8.head_dim, w8.chunk_tokens, w8.cond_tokens, w8.window) == \
+            (w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window):
+        # a bounded sample of heads (one per thread), scaled to the whole call
+        h8 = min(w8.heads, threads)
+        t8, a8, kw8, kv8, _ = _oracle_call(w8, seed_dist, fp8=True, heads=h8)
+        q8, ck8, cv8, hk8, hv8, k8, v8, sc8 = a8
+
+        def one_head8(h):
+            sl = lambda x: head_slice(x, h)
+            O1.chunk_attention(sl(q8), sl(ck8), sl(cv8), [sl(x) for x in hk8],
+                               [sl(x) for x in hv8], sl(k8), sl(v8), sc8)
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            def run8():
+                list(ex.map(one_head8, range(h8)))
+            if threadpool_limits is not None:
+                with threadpool_limits(limits=1):
+                    c8, d8 = _time_calls(run8, seconds / 2)
+            else:
+                c8, d8 = _time_calls(run8, seconds / 2)
+        call8 = d8 / c8 * w8.heads / h8
+        out["legs"]["fp8"] = {
+            "value": attn_flops(w8, kv8) / call8 / 1e12, "unit": "TFLOP/s",
+            "cores": int(threads), "chunks_per_s": 1.0 / call8,
+            "sample": f"fp8 steady chunk t={t8} ({kv8} keys), oracle on the dequantised "
+                      f"K/V, {h8} of {w8.heads} heads on {threads} threads, {c8} times in "
+                      f"{d8:.2f} s, scaled to the whole call"}
+    # full depth: 48 layers x 2 denoise steps per chunk, extrapolated
+    wd = synth.WORKLOADS["depth"]
+    per_chunk = wd.layers * wd.steps
+    out["legs"]["depth_extrapolated"] = {
+        "chunks_per_s": calls / dt / per_chunk, "unit": "chunks/s", "extrapolated": True,
+        "sample": f"{per_chunk} x the {w.name} oracle call above "
+                  f"({wd.layers} layers x {wd.steps} denoise steps), not run"}
+    return out
 
 
 def _cpu_model() -> str:
@@ -338,6 +446,11 @@ def run_stream_bench(w, args, device, flat: bool):
         end.record(stream)
         host_s = time.perf_counter() - h0   # enqueue time (the GPU runs behind)
         torch.cuda.synchronize()
+        # the shader clock under this load: the same chunks keep running
+        # (untimed, after the timed region) while another thread asks
+        # rocm-smi for the current clock
+        clock = None if args.no_clock else clock_under_load(
+            lambda tt: [chunk(tt + i, False) for i in range(4)], t)
     finally:
         gc.enable()
     tele_after = gpu_telemetry() if flat else None
@@ -359,6 +472,7 @@ def run_stream_bench(w, args, device, flat: bool):
         "calls_per_step": (w.steps + (1 if args.clean_pass else 0)) * w.layers,
         "writes_per_step": (w.steps + 1) * w.layers,
         "telemetry": {"before_warmup": tele_before, "after": tele_after} if flat else None,
+        "clock": clock,
     }
     if args.copy_calib_mib:
         # a plain device copy of known size, for scaling the HBM byte counters
@@ -420,6 +534,48 @@ def gpu_telemetry():
             if "sclk" in k.lower() or "temperature" in k.lower()}
 
 
+def sclk_mhz(tele) -> float | None:
+    """The current shader clock in MHz from rocm-smi's JSON fields (the first
+    'sclk' field holding a value in MHz)."""
+    import re
+    if not tele:
+        return None
+    for k, v in tele.items():
+        if "sclk" in k.lower():
+            m = re.search(r"(\d+(?:\.\d+)?)\s*mhz", str(v), flags=re.I)
+            if m:
+                return float(m.group(1))
+    return None
+
+
+def clock_under_load(run_chunks, t0: int, min_s: float = 1.0, max_s: float = 25.0):
+    """Keeps the GPU busy with `run_chunks(t)` (untimed; 4 chunks per call)
+    while a second thread reads the shader clock with rocm-smi.  Returns
+    {"sclk_mhz": ..., "telemetry": {...}} or None."""
+    import threading
+    import torch
+    got = {}
+
+    def probe():
+        time.sleep(0.3)          # let the load settle first
+        got["tele"] = gpu_telemetry()
+    th = threading.Thread(target=probe, daemon=True)
+    start = time.perf_counter()
+    th.start()
+    t = t0
+    while True:
+        run_chunks(t)
+        t += 4
+        torch.cuda.synchronize()
+        el = time.perf_counter() - start
+        if (not th.is_alive() and el >= min_s) or el >= max_s:
+            break
+    th.join(timeout=1.0)
+    tele = got.get("tele")
+    mhz = sclk_mhz(tele)
+    return {"sclk_mhz": mhz, "telemetry": tele} if tele else None
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_720p_traffic.json")
 
 
@@ -464,6 +620,8 @@ def main() -> int:
     ap.add_argument("--rope", action="store_true",
                     help="rotary encoding fused into the cache writes and the Q load "
                          "(one angle table per chunk)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip reading the shader clock under load after the timed region")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -580,13 +738,22 @@ def main() -> int:
             "per_launch_flops": flops,
         },
     }
+    # the published peak assumes 2.4 GHz; under this load the clock reads lower
+    mhz = (r.get("clock") or {}).get("sclk_mhz")
+    out["sclk_mhz_under_load"] = mhz
+    if mhz:
+        peak_at = peak * mhz / 2400.0
+        out["roofline"]["measured_clock_mhz"] = mhz
+        out["roofline"]["peak_at_measured_clock"] = round(peak_at, 1)
+        out["roofline"]["frac_at_measured_clock"] = round(achieved / peak_at, 4)
     if flat:
         out["flatness"] = flatness(r["step_ms"], r["attn_ms_all"], w.window)
         out["flatness"]["telemetry"] = r.get("telemetry")
     if "copy_calib" in r:
         out["copy_calib"] = r["copy_calib"]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.dist)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.dist,
+                                           legs=w.name == "720p")
     print(json.dumps(out), flush=True)
     return 0
 

@@ -300,6 +300,17 @@ __device__ __forceinline__ void cursor_next(const AttnArgs& a, TileCursor& c, in
   }
 }
 
+// x, as a value the compiler cannot see through.  Addresses derived from it
+// are computed where they are used: left to itself, the compiler hoists the
+// per-lane addresses of the code after the step loop (partial stores, vote
+// slots) out of every loop and keeps them in VGPRs across the whole loop,
+// which at this register budget spilled other long-lived values to scratch.
+template <typename T>
+__device__ __forceinline__ T opaque(T x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // workgroup-wide OR of two per-wave flags (every wave must take the same path
 // when the paths contain barriers)
 __device__ __forceinline__ void vote2(int (&slot)[kWaves][2], int wave, int lane, bool p0,
@@ -311,10 +322,11 @@ __device__ __forceinline__ void vote2(int (&slot)[kWaves][2], int wave, int lane
   }
   __syncthreads();
   any0 = any1 = false;
+  const int z = opaque(0);
 #pragma unroll
   for (int v = 0; v < kWaves; ++v) {
-    any0 = any0 || slot[v][0];
-    any1 = any1 || slot[v][1];
+    any0 = any0 || slot[v + z][0];
+    any1 = any1 || slot[v + z][1];
   }
 }
 
@@ -348,6 +360,7 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
                                              unsigned& s_ticket, const Split& sp) {
   constexpr int kDB = D / 32;
   const int tid = threadIdx.x;
+  lane = opaque(lane);
   const int col = lane & 31;
   const int half = lane >> 5;
   const long long rs = static_cast<long long>(r) * a.ntiles;

@@ -37,6 +37,29 @@ def test_cpu_baseline_reports_the_oracle_on_a_bounded_sample():
     assert cb["value"] == pytest.approx(flops / cb["seconds"] / 1e12, rel=1e-9)
 
 
+def test_cpu_baseline_legs():
+    # one core, the fp8 configuration's oracle and the full-depth
+    # extrapolation, each labelled; the fp8 leg needs the 720p shape, so on
+    # the tiny workload it is absent
+    import bench
+    import synth
+    w = synth.WORKLOADS["tiny"]
+    cb = bench.cpu_baseline(w, 0.2, legs=True)
+    legs = cb["legs"]
+    assert legs["single_core"]["cores"] == 1 and legs["single_core"]["value"] > 0
+    assert "fp8" not in legs
+    d = legs["depth_extrapolated"]
+    assert d["extrapolated"] is True and d["unit"] == "chunks/s"
+    assert d["chunks_per_s"] == pytest.approx(cb["chunks_per_s"] / 96)
+
+
+def test_shader_clock_parsing():
+    import bench
+    assert bench.sclk_mhz({"sclk clock speed:": "(2100Mhz)", "sclk clock level:": "1"}) == 2100
+    assert bench.sclk_mhz({"Temperature (Sensor edge) (C)": "41.0"}) is None
+    assert bench.sclk_mhz(None) is None
+
+
 @pytest.mark.gpu
 def test_bench_line_on_the_tiny_workload():
     print("bench.py --config tiny --steps 3", flush=True)
@@ -63,3 +86,11 @@ def test_bench_line_on_the_tiny_workload():
     # frac is printed with 4 decimals
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) <= 5e-5 + 1e-9
     assert "cpu_baseline" not in j
+    # the shader clock read under load (None if rocm-smi gives none), and the
+    # roofline fraction at that clock
+    assert "sclk_mhz_under_load" in j
+    mhz = j["sclk_mhz_under_load"]
+    if mhz:
+        assert 500 <= mhz <= 3000
+        assert rf["frac_at_measured_clock"] == pytest.approx(
+            rf["achieved"] / (rf["peak"] * mhz / 2400), abs=1e-4)
