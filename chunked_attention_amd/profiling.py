@@ -79,6 +79,19 @@ def steady_attention(dirname: str, steady: int):
     return short_name(last[-1]["Kernel_Name"]), statistics.mean(durs), len(durs)
 
 
+def steady_mean_us(dirname: str, kernel: str, steady: int) -> float:
+    """mean duration (us) of the last `steady` dispatches of `kernel` in a
+    kernel trace"""
+    path = _one(dirname, "*kernel_trace.csv")
+    rows = [r for r in csv.DictReader(open(path)) if _is(kernel, r["Kernel_Name"])]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    last = rows[-steady:]
+    if not last:
+        raise SystemExit(f"no {kernel} dispatches in {path}")
+    return statistics.mean((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                           for r in last)
+
+
 def stats_md(dirname: str, cmd: str, steady: int = 0) -> str:
     path = _one(dirname, "*kernel_stats.csv")
     rows = list(csv.DictReader(open(path)))
@@ -130,19 +143,24 @@ CUS, XCDS, SIMDS = 256, 8, 4
 BF16_FLOPS_PER_SIMD_CYCLE = 1024
 
 
-def counters_md(dirs, cmds, steady: int, flops: float, workload: str) -> str:
+# dense fp8 (E4M3) MFMAs do twice the FLOPs per SIMD-cycle of bf16 ones
+FLOPS_PER_SIMD_CYCLE = {ATTN: BF16_FLOPS_PER_SIMD_CYCLE, ATTN8: 2 * BF16_FLOPS_PER_SIMD_CYCLE}
+
+
+def counters_md(dirs, cmds, steady: int, flops: float, workload: str, kernel: str = ATTN) -> str:
     vals, durs = {}, []
     for d in dirs:
-        attn = [v for _, v in sorted(_dispatches(d).items()) if ATTN in v[0]][-steady:]
+        attn = [v for _, v in sorted(_dispatches(d).items())
+                if kernel in v[0] and not (kernel == ATTN and ATTN8 in v[0])][-steady:]
         if not attn:
-            raise SystemExit(f"no attention dispatches in {d}")
+            raise SystemExit(f"no {kernel} dispatches in {d}")
         durs += [dur for _, dur, _ in attn]
         for name in attn[0][2]:
             vals[name] = statistics.mean(c[name] for _, _, c in attn)
     dur_s = statistics.mean(durs) * 1e-9
-    out = ["# Counters of the attention kernel (rocprofv3 --pmc)", "",
+    out = [f"# Counters of {kernel} (rocprofv3 --pmc)", "",
            f"Workload: {workload}.  Each counter summed over its hardware instances and "
-           f"averaged over the last {steady} attention dispatches of its run; one run per "
+           f"averaged over the last {steady} {kernel} dispatches of its run; one run per "
            f"counter set.", "", "Commands (from the repository root):", "", "```", *cmds,
            "```", "", "| counter | per dispatch |", "|---|---|"]
     out += [f"| {k} | {v:,.0f} |" for k, v in sorted(vals.items())]
@@ -159,9 +177,10 @@ def counters_md(dirs, cmds, steady: int, flops: float, workload: str) -> str:
             derived.append(f"- Matrix pipes busy: SQ_VALU_MFMA_BUSY_CYCLES / ({CUS} CUs x "
                            f"{SIMDS} SIMDs x cycles) = {100 * busy / simd_cycles:.1f}%.")
             if flops:
-                need = flops / BF16_FLOPS_PER_SIMD_CYCLE
+                per = FLOPS_PER_SIMD_CYCLE.get(kernel, BF16_FLOPS_PER_SIMD_CYCLE)
+                need = flops / per
                 derived.append(f"- The algorithmic {flops / 1e9:.2f} GFLOP need {need:,.0f} "
-                               f"busy SIMD-cycles at {BF16_FLOPS_PER_SIMD_CYCLE} FLOP each: "
+                               f"busy SIMD-cycles at {per} FLOP each: "
                                f"{100 * need / busy:.1f}% of the busy cycles (the rest: "
                                f"padded tiles and rows).")
     if "SQ_LDS_BANK_CONFLICT" in vals and vals.get("SQ_INSTS_LDS"):
@@ -175,15 +194,19 @@ def counters_md(dirs, cmds, steady: int, flops: float, workload: str) -> str:
     return "\n".join(out)
 
 
-def traffic(fetch_dir, write_dir, calib_mib, steady):
+def _is(kernel: str, name: str) -> bool:
+    return kernel in name and not (kernel == ATTN and ATTN8 in name)
+
+
+def traffic(fetch_dir, write_dir, calib_mib, steady, kernel: str = ATTN):
     calib_bytes = calib_mib << 20
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter(d, counter)
-        attn = [v for n, v in rows if ATTN in n][-steady:]
+        attn = [v for n, v in rows if _is(kernel, n)][-steady:]
         cal = [v for n, v in rows if CALIB in n]
         if not attn or not cal:
-            raise SystemExit(f"{counter}: no attention or calibration dispatches in {d}")
+            raise SystemExit(f"{counter}: no {kernel} or calibration dispatches in {d}")
         kib_attn = statistics.mean(attn)
         kib_cal = statistics.median(cal)
         factor = calib_bytes / (kib_cal * 1024.0)
@@ -209,6 +232,7 @@ def main(argv=None):
     c.add_argument("--steady", type=int, default=3)
     c.add_argument("--flops", type=float, default=0.0, help="algorithmic FLOPs per call")
     c.add_argument("--workload", default="720p steady chunk (8356 keys)")
+    c.add_argument("--kernel", default=ATTN, help="kernel name (substring) to summarise")
     c.add_argument("--out", required=True)
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
@@ -218,7 +242,13 @@ def main(argv=None):
     b.add_argument("--cmd-fetch", required=True)
     b.add_argument("--cmd-write", required=True)
     b.add_argument("--workload", default="720p steady chunk (8356 keys)")
-    b.add_argument("--out", required=True)
+    b.add_argument("--kernel", default=ATTN, help="kernel name (substring) to summarise")
+    b.add_argument("--stats-dir", default=None,
+                   help="kernel-trace run of the same command: mean duration of the same "
+                        "dispatches, for GB/s")
+    b.add_argument("--algo-bytes", type=float, default=0.0,
+                   help="algorithmic bytes per dispatch (reads + writes)")
+    b.add_argument("--out", default=None, help="JSON record (the bf16 attention kernel)")
     b.add_argument("--md", required=True)
     args = ap.parse_args(argv)
     if args.what == "stats":
@@ -226,30 +256,42 @@ def main(argv=None):
         return 0
     if args.what == "counters":
         open(args.out, "w").write(counters_md(args.dirs, args.cmd, args.steady, args.flops,
-                                              args.workload))
+                                              args.workload, args.kernel))
         return 0
-    res, total = traffic(args.fetch, args.write, args.calib_mib, args.steady)
+    res, total = traffic(args.fetch, args.write, args.calib_mib, args.steady, args.kernel)
     sha = kernel_code_digest()
-    rec = {"kernel": ATTN, "workload": args.workload, "kernel_code_sha256": sha,
-           "hbm_bytes_per_launch": round(total), "counters": res,
-           "commands": {"FETCH_SIZE": args.cmd_fetch, "WRITE_SIZE": args.cmd_write}}
-    json.dump(rec, open(args.out, "w"), indent=1)
+    if args.out:
+        rec = {"kernel": args.kernel, "workload": args.workload, "kernel_code_sha256": sha,
+               "hbm_bytes_per_launch": round(total), "counters": res,
+               "commands": {"FETCH_SIZE": args.cmd_fetch, "WRITE_SIZE": args.cmd_write}}
+        json.dump(rec, open(args.out, "w"), indent=1)
     f, wr = res["FETCH_SIZE"], res["WRITE_SIZE"]
-    md = ["# HBM traffic of the attention kernel (rocprofv3 counters)", "",
+    md = [f"# HBM traffic of {args.kernel} (rocprofv3 counters)", "",
           f"Workload: {args.workload}.  Counters in KiB per dispatch, averaged over the "
-          f"last {f['attn_dispatches']} attention dispatches (steady state); each counter "
+          f"last {f['attn_dispatches']} {args.kernel} dispatches (steady state); each counter "
           f"is scaled by bytes / reading of a plain elementwise kernel that reads and writes "
           f"{args.calib_mib} MiB once.", "",
           "Commands (from the repository root):", "", "```", args.cmd_fetch, args.cmd_write,
           "```", "",
-          "| counter | attention KiB/dispatch | calibration KiB/dispatch | scale | bytes/launch |",
+          "| counter | kernel KiB/dispatch | calibration KiB/dispatch | scale | bytes/launch |",
           "|---|---|---|---|---|",
           f"| FETCH_SIZE | {f['attn_kib_per_dispatch']:.0f} | {f['calib_kib_per_dispatch']:.0f} | "
           f"{f['scale']:.4f} | {f['attn_bytes'] / 1e6:.1f} MB |",
           f"| WRITE_SIZE | {wr['attn_kib_per_dispatch']:.0f} | {wr['calib_kib_per_dispatch']:.0f} | "
           f"{wr['scale']:.4f} | {wr['attn_bytes'] / 1e6:.1f} MB |",
-          "", f"Total HBM bytes per launch: {total / 1e6:.1f} MB.  Kernel code sha256 "
-          f"{sha[:16]}...", ""]
+          "", f"Total HBM bytes per launch: {total / 1e6:.1f} MB."]
+    if args.algo_bytes:
+        md.append(f"Algorithmic bytes per launch: {args.algo_bytes / 1e6:.1f} MB "
+                  f"(measured / algorithmic = {total / args.algo_bytes:.2f}).")
+    if args.stats_dir:
+        us = steady_mean_us(args.stats_dir, args.kernel, args.steady)
+        md.append(f"Mean duration of the same dispatches in a kernel-trace run of the same "
+                  f"command: {us:.2f} us, i.e. {total / (us * 1e-6) / 1e9:,.0f} GB/s measured"
+                  + (f" and {args.algo_bytes / (us * 1e-6) / 1e9:,.0f} GB/s algorithmic"
+                     if args.algo_bytes else "") + " against the 8,000 GB/s HBM peak.")
+    if args.kernel == ATTN:
+        md.append(f"Kernel code sha256 {sha[:16]}... (the bf16 attention kernel's sources).")
+    md.append("")
     open(args.md, "w").write("\n".join(md))
     print(json.dumps({"hbm_bytes_per_launch": round(total)}))
     return 0

@@ -73,15 +73,15 @@ class StreamRun:
             ring.ref(rk.cuda(), rv.cuda())
 
     def _ref(self, x):
+        # the sampled heads first: the fp8 scales are per (head, segment), so
+        # the round trip of a head does not depend on the other heads
         if x is None:
             return None
-        if self.fp8:
-            y = fp8_roundtrip_tokens(x)
-        else:
-            y = O1.as_f64(x)
         if self.heads is not None:
-            y = y[:, self.heads]
-        return y
+            x = x[:, self.heads]
+        if self.fp8:
+            return fp8_roundtrip_tokens(x)
+        return O1.as_f64(x)
 
     def chunk(self, t: int, check: bool = True, lse: bool = False):
         """Stage + attend every step, commit, evict.  Returns per-step
@@ -95,7 +95,8 @@ class StreamRun:
             if src:
                 sk, sv = self.s.kv_src(t, step)
                 q = torch.cat([q, self.s.q_src(t, step)])
-            self.last_vmax = float(np.abs(self._ref(v)).max())
+            if check:
+                self.last_vmax = float(np.abs(self._ref(v)).max())
             if src:
                 self.ring.stage(torch.cat([k, sk]).cuda(), torch.cat([v, sv]).cuda())
             else:

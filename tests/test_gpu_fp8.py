@@ -141,6 +141,23 @@ def test_fp8_config_stream_sampled(dist):
         print(f"fp8 cfg {dist} t={t}: max-abs {st['max_abs']:.2e} rel-L2 {st['rel_l2']:.2e}")
 
 
+def test_fp8_config_whole_stream_sampled_chunks():
+    # the whole fp8 configuration stream (32 chunks, unique inputs per chunk):
+    # every chunk staged, attended, committed and evicted on the GPU; the
+    # oracle checks chunks 4, 13, 22 and 31 (steady state, far from the
+    # start) on heads 0, 17 and 39
+    w = synth.WORKLOADS["fp8"]
+    heads = [0, 17, 39]
+    checked = {4, 13, 22, 31}
+    run = StreamRun(synth.Stream(w, "baseline"), fp8_ring(w), fp8=True, heads=heads)
+    for t in range(w.chunks):
+        (o, ref, st), = run.chunk(t, check=t in checked)
+        if t in checked:
+            check_fp8(st, f"fp8 cfg t={t}")
+            print(f"fp8 cfg t={t}: max-abs {st['max_abs']:.2e} rel-L2 {st['rel_l2']:.2e}")
+    assert run.ring.info().chunk == w.chunks
+
+
 def test_fp8_three_frame_chunk_whole_rows_first():
     # 4860-query chunks on an E4M3 ring (40 heads x 128, W = 3, 24556 keys
     # from chunk 4): 1520 rows of 384 tiles over 512 workgroups, so the
