@@ -42,7 +42,7 @@ def check_mask(zs, ze, tau=None, keep=None):
 
 @pytest.mark.parametrize("frames,grid,channels", [
     (1, (8, 8), 16), (1, (30, 54), 16), (3, (30, 54), 16), (1, (30, 54), 48),
-    (1, (128, 128), 4), (1, (1, 1), 1), (1, (10, 100), 4096),
+    (1, (128, 128), 4), (1, (1, 1), 1), (1, (10, 100), 4096), (1, (50, 60), 24),
 ])
 def test_edit_mask_bit_exact(frames, grid, channels):
     zs, ze = synth.edit_latents(3, 0, grid, frames, channels)
