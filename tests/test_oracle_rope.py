@@ -1,8 +1,11 @@
 """Pins for O5 (rotary encoding of Q and K), CPU only.  Each test pins the
 oracle to something other than itself: complex multiplication (numpy's
-complex128), closed forms, the relative-position property of RoPE, and
-torch's float32 CPU arithmetic for the stored bf16 values."""
+complex128), closed forms, the relative-position property of RoPE, and for
+the stored bf16 values torch's float32 CPU arithmetic and a rounding written
+from the definition on exact rationals (with a case where rounding once,
+straight to bf16, would give a different value)."""
 import math
+from fractions import Fraction
 
 import numpy as np
 import torch
@@ -85,3 +88,77 @@ def test_stored_values_are_float32_ops_rounded_to_bf16():
     exact = O5.rotate(x, tab.numpy().astype(np.float64))
     assert np.abs(got.to(torch.float64).numpy() - exact).max() <= \
         2.0 ** -8 * np.abs(exact).max()
+
+
+# Round to nearest, ties to even, into a binary format with p significand
+# bits and smallest normal exponent emin (subnormals below it), written from
+# the definition on exact rationals: independent of numpy's and torch's
+# float32 and bf16 arithmetic.
+def _rne(q: Fraction, p: int, emin: int) -> Fraction:
+    if q == 0:
+        return Fraction(0)
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, emin) - (p - 1))
+    m = a / quantum
+    n = m.numerator // m.denominator
+    r = m - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return (1 if q > 0 else -1) * n * quantum
+
+
+def _f32(q):
+    return _rne(q, 24, -126)
+
+
+def _bf16(q):
+    return _rne(q, 8, -126)
+
+
+def _stored_exact(xe, xo, c, s):
+    """the pair's stored values: float32 products, float32 difference / sum,
+    then bf16, every rounding on exact rationals"""
+    xe, xo, c, s = (Fraction(float(v)) for v in (xe, xo, c, s))
+    a, b = _f32(xe * c), _f32(xo * s)
+    even = _bf16(_f32(a - b))
+    a, b = _f32(xe * s), _f32(xo * c)
+    odd = _bf16(_f32(a + b))
+    return even, odd
+
+
+def test_stored_values_match_exact_rational_rounding():
+    # random pairs and angles
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn(6, 2, 32, generator=g).to(torch.bfloat16)
+    ang = torch.rand(6, 16, generator=g, dtype=torch.float64) * 6.3 - 3.15
+    tab = torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).to(torch.float32).numpy()
+    got = O5.rotate_stored(x, tab).to(torch.float64).numpy()
+    xf = x.to(torch.float32).numpy()
+    for r in range(x.shape[0]):
+        for h in range(x.shape[1]):
+            for i in range(x.shape[2] // 2):
+                even, odd = _stored_exact(xf[r, h, 2 * i], xf[r, h, 2 * i + 1],
+                                          tab[r, i, 0], tab[r, i, 1])
+                assert Fraction(float(got[r, h, 2 * i])) == even
+                assert Fraction(float(got[r, h, 2 * i + 1])) == odd
+
+
+def test_stored_values_round_twice():
+    # x = (1, 2^-10), (cos, sin) = (1 + 2^-8, -2^-20): the exact even
+    # output is 1 + 2^-8 + 2^-30.  Rounded straight to bf16 it would be
+    # 1 + 2^-7 (above the midpoint); through float32 it is first the
+    # midpoint 1 + 2^-8, which bf16 rounds to even: 1.  The odd output is
+    # sin + 2^-10 cos = -2^-20 + 2^-10 + 2^-18 (float32 exact), bf16 2^-10.
+    x = torch.tensor([[[1.0, 2.0 ** -10]]], dtype=torch.bfloat16)
+    tab = np.array([[[1.0 + 2.0 ** -8, -2.0 ** -20]]], dtype=np.float32)
+    got = O5.rotate_stored(x, tab).to(torch.float64).numpy()[0, 0]
+    assert got[0] == 1.0
+    assert _bf16(Fraction(1) + Fraction(1, 2 ** 8) + Fraction(1, 2 ** 30)) == 1 + Fraction(1, 2 ** 7)
+    assert (Fraction(float(got[0])), Fraction(float(got[1]))) == \
+        _stored_exact(1.0, 2.0 ** -10, tab[0, 0, 0], tab[0, 0, 1])
+    assert got[1] == 2.0 ** -10
