@@ -69,6 +69,35 @@ def test_edit_mask_ties_and_nan():
         check_mask(zs, ze, tau=tau)
 
 
+def test_edit_mask_ties_across_rounds():
+    # 5000 tokens (five rounds of 1024 owner threads, a part-filled last
+    # round) holding only five distinct distances, spread by a multiplicative
+    # hash so that every tie group spans every round and wave: the top-k cut
+    # falls inside a tie group, and the lowest indices of the group must win
+    # across rounds; three NaN distances sit in later rounds
+    tokens = 5000
+    idx = torch.arange(tokens)
+    level = (idx * 7919) % 5                      # 0..4
+    zs = torch.zeros(tokens, 3, dtype=torch.bfloat16)
+    ze = torch.zeros(tokens, 3, dtype=torch.float32)
+    ze[:, 0] = level.to(torch.float32)            # distance level^2
+    ze = ze.to(torch.bfloat16)
+    ze[1500, 1] = float("nan")
+    ze[3071, 2] = float("nan")
+    ze[4999, 0] = float("nan")
+    counts = [int((level == v).sum()) for v in range(5)]
+    print(f"mask ties across rounds, level counts {counts}", flush=True)
+    above = 0
+    keeps = {0, 1, tokens - 3, tokens}
+    for v in (4, 3, 2, 1, 0):
+        keeps |= {above + 1, above + counts[v] // 2, above + counts[v] - 1}
+        above += counts[v]
+    for keep in sorted(k for k in keeps if 0 <= k <= tokens + 5):
+        check_mask(zs, ze, keep=keep)
+    for tau in (0.0, 1.0, 1.5, 3.5):
+        check_mask(zs, ze, tau=tau)
+
+
 def test_edit_mask_deep_digits():
     # distances 1 + (k 2^-20)^2 (k = token mod 256): equal in their top 40
     # bits, so the top-k select runs through most digits before a bin holds
