@@ -278,7 +278,7 @@ void attn_fwd_fp8(const AttnArgs a) {
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
       int pv_seg = -1;
       f32x16_t sacc[2];
-      int pf[2][4];   // E4M3 P of the two half tiles: byte (i%4) of word i/4
+      int pf[2][4] = {};   // E4M3 P of the two half tiles: byte (i%4) of word i/4
 
       // softmax multiplier of the tile whose scores are being consumed
       auto ceff = [&](const TileCursor& c) { return cq * a.seg[c.s].ks[h]; };
@@ -349,7 +349,9 @@ void attn_fwd_fp8(const AttnArgs a) {
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[4 * v + 1], c_eff, neg_m));
           const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[4 * v + 2], c_eff, neg_m));
           const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[4 * v + 3], c_eff, neg_m));
-          pf[HH][v] = pack8<true>(p2, p3, pack8<false>(p0, p1, 0));
+          // the second conversion overwrites bytes 2-3 of the first's result, so
+          // the first may write into last tile's (dead) word: no zeroing copy
+          pf[HH][v] = pack8<true>(p2, p3, pack8<false>(p0, p1, pf[HH][v]));
         }
       };
       auto tile = [&](auto u_tag) {
