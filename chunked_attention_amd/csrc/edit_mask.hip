@@ -217,7 +217,10 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
     const uint16_t* __restrict__ zs, const uint16_t* __restrict__ ze, int tokens, int channels,
     double tau2, int keep, bool vec, int* __restrict__ rows, int* __restrict__ count) {
   constexpr int kPasses = 8;   // 8-bit digits of a 64-bit key
-  __shared__ unsigned long long keys[kTopK ? KVC_MAX_MASK_TOKENS : 1];   // [round][thread]
+  // top-k mode: the keys, [round][thread] for the tokens that exist (dynamic
+  // LDS of tokens * 8 bytes, so that a small call leaves room on its CU for
+  // other kernels' workgroups)
+  extern __shared__ unsigned long long keys[];
   __shared__ unsigned hist[kTopK ? kPasses : 1][256];                  // one per pass
   __shared__ int table[2][kRounds * kWaves];
   __shared__ unsigned long long wand[kWaves], wor[kWaves];
@@ -369,6 +372,12 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
 }  // namespace
 
 kvc_status launch_edit_mask(const EditMaskDesc& d, void* stream) {
+  // the top-k kernel's keys may take up to 128 KB of dynamic LDS
+  static const hipError_t lds_ok = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(edit_mask_kernel<true>),
+      hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(sizeof(unsigned long long) * KVC_MAX_MASK_TOKENS));
+  if (lds_ok != hipSuccess) return KVC_E_DEVICE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* zs = static_cast<const uint16_t*>(d.z_src);
   const auto* ze = static_cast<const uint16_t*>(d.z_edit);
@@ -380,8 +389,9 @@ kvc_status launch_edit_mask(const EditMaskDesc& d, void* stream) {
     hipLaunchKernelGGL(edit_mask_kernel<false>, dim3(1), dim3(kThreads), 0, s, zs, ze, d.tokens,
                        d.channels, t * t, 0, vec, d.rows, d.count);
   else
-    hipLaunchKernelGGL(edit_mask_kernel<true>, dim3(1), dim3(kThreads), 0, s, zs, ze, d.tokens,
-                       d.channels, 0.0, d.keep, vec, d.rows, d.count);
+    hipLaunchKernelGGL(edit_mask_kernel<true>, dim3(1), dim3(kThreads),
+                       sizeof(unsigned long long) * static_cast<size_t>(d.tokens), s, zs, ze,
+                       d.tokens, d.channels, 0.0, d.keep, vec, d.rows, d.count);
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_DEVICE;
 }
 
