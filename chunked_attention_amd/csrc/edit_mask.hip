@@ -32,6 +32,10 @@
 //   3. compact: the rank of a chosen token among the chosen ones in index
 //      order is a ballot count within its wave plus a prefix over the
 //      (round, wave) counts, which every wave scans for itself.
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
 #include "device_common.hpp"
 #include "kvc_internal.hpp"
 
@@ -371,13 +375,28 @@ __global__ __launch_bounds__(kThreads) void edit_mask_kernel(
 
 }  // namespace
 
+// The top-k kernel's keys may take up to 128 KB of dynamic LDS: allow it
+// once per device (the first call on each device).
+static kvc_status allow_mask_lds() {
+  static std::mutex mu;
+  static std::vector<int> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVC_E_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (std::find(done.begin(), done.end(), dev) != done.end()) return KVC_OK;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(edit_mask_kernel<true>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(sizeof(unsigned long long) * KVC_MAX_MASK_TOKENS)) !=
+      hipSuccess)
+    return KVC_E_DEVICE;
+  done.push_back(dev);
+  return KVC_OK;
+}
+
 kvc_status launch_edit_mask(const EditMaskDesc& d, void* stream) {
-  // the top-k kernel's keys may take up to 128 KB of dynamic LDS
-  static const hipError_t lds_ok = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(edit_mask_kernel<true>),
-      hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(sizeof(unsigned long long) * KVC_MAX_MASK_TOKENS));
-  if (lds_ok != hipSuccess) return KVC_E_DEVICE;
+  if (d.keep >= 0) {
+    if (kvc_status st = allow_mask_lds()) return st;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const auto* zs = static_cast<const uint16_t*>(d.z_src);
   const auto* ze = static_cast<const uint16_t*>(d.z_edit);
