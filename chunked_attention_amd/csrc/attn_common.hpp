@@ -336,7 +336,9 @@ __device__ __forceinline__ void vote2(int (&slot)[kWaves][2], int wave, int lane
 // the row sum that normalises O (the lse output is m_run + log2 l_tot, in
 // natural-log units).  A piece that covers its whole row writes O / l (bf16)
 // and lse; otherwise the last piece of the row to arrive merges every
-// piece's partial in piece order, and the others store theirs.
+// piece's partial in piece order, and the others store theirs.  epoch is the
+// call's epoch (a.epoch; a caller at the register limit may pass a copy it
+// keeps in a scalar register).
 //
 // Protocol (every word tagged with the call's epoch, so nothing is reset and
 // stale words from earlier calls are told apart):
@@ -357,7 +359,8 @@ template <int D, bool kLse>
 __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)[D / 32],
                                              float m_run, float l_tot, int r, int h, int qbase,
                                              bool first_piece, int w, int wave, int lane,
-                                             unsigned& s_ticket, const Split& sp) {
+                                             unsigned& s_ticket, const Split& sp,
+                                             const unsigned epoch) {
   constexpr int kDB = D / 32;
   const int tid = threadIdx.x;
   lane = opaque(lane);
@@ -372,11 +375,11 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
     __syncthreads();
     if (tid == 0) {
       unsigned long long* word = a.arrive + r;
-      const unsigned long long mine = static_cast<unsigned long long>(a.epoch) << 32;
+      const unsigned long long mine = static_cast<unsigned long long>(epoch) << 32;
       unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       unsigned long long next;
       do {
-        next = (old >> 32) == a.epoch ? old + 1 : mine | 1u;
+        next = (old >> 32) == epoch ? old + 1 : mine | 1u;
       } while (!__hip_atomic_compare_exchange_strong(word, &old, next, __ATOMIC_RELAXED,
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       s_ticket = static_cast<unsigned>(next);
@@ -402,7 +405,7 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
       __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): stores complete
       __syncthreads();
       if (tid == 0)
-        __hip_atomic_store(a.tags + slot, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.tags + slot, epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       return;
     }
     // wait until every other piece has stored its partial (they have all
@@ -418,7 +421,7 @@ __device__ __forceinline__ void finish_piece(const AttnArgs& a, f32x16_t (&oacc)
         if (ow == w) continue;
         const int oslot = 2 * ow + (range_begin(ow, sp) >= rs ? 0 : 1);
         while (__hip_atomic_load(a.tags + oslot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
-               a.epoch) {
+               epoch) {
           if (--budget <= 0) {
             missing = 1;
             break;

@@ -407,7 +407,7 @@ void attn_fwd_bf16(const AttnArgs a) {
     // log of the same sum O is divided by (within ln(1 + 2^-8) of the sum
     // of the unrounded p, each weight being rounded to bf16 once)
     finish_piece<D, kLse>(a, oacc, m_ref, l_tot, r, h, qbase, first_piece, w, wave, lane,
-                          s_ticket, sp);
+                          s_ticket, sp, a.epoch);
   };
 
   // The pieces of this workgroup's range (one per row it touches).

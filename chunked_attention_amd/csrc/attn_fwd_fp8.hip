@@ -87,6 +87,16 @@ __device__ __forceinline__ int pack8(float x, float y, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(x, y, old, kHigh);
 }
 
+// This wave's lane index, computed afresh where it is called (volatile, so
+// the compiler can neither merge it with another call nor hoist it): at the
+// register limit, per-lane values kept from the prologue across the piece
+// loop would otherwise be spilled.
+__device__ __forceinline__ int lane_now() {
+  int r;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+  return r;
+}
+
 template <int D, bool kLse, bool kRope, bool kRowsFirst>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_fp8(const AttnArgs a) {
@@ -206,8 +216,13 @@ void attn_fwd_fp8(const AttnArgs a) {
   // one piece: tiles [t0, t1) of row r; first_piece if it holds the first
   // tile of this workgroup's range (the partial slot it uses if split)
   auto piece = [&](const int r, const int t0, const int t1, const bool first_piece) {
-    const int h = r / sp.nqt;
-    const int qbase = (r - h * sp.nqt) * kBq + wave * kQW;
+    // the row count and the epoch are read as scalars in every piece: the
+    // division's reciprocal and a vector copy of the epoch, hoisted out of
+    // the piece loop, would each take a register across it
+    int nqt = sp.nqt;
+    asm volatile("" : "+s"(nqt));
+    const int h = r / nqt;
+    const int qbase = (r - h * nqt) * kBq + wave * kQW;
 
     // Q^T as B operands: lane holds query qbase + col, byte j of k-step ks
     // = feature ks*64 + half*32 + j.  q / s_q = Q8hi + Q8lo / 16 (E4M3 of
@@ -216,10 +231,13 @@ void attn_fwd_fp8(const AttnArgs a) {
     i32x8_t q8[kKS], q8lo[kKS];
     float cq;   // scale * log2(e) * s_q
     {
-      const int g = query_row(a, sp, qbase + col);
+      const int ln = lane_now();
+      const int qcol = ln & 31;
+      const int qhalf = ln >> 5;
+      const int g = query_row(a, sp, qbase + qcol);
       float qv[kKS][32];
       const uint16_t* qrow = a.q + (static_cast<size_t>(g < 0 ? 0 : g) * a.heads + h) * D +
-                             half * 32;
+                             qhalf * 32;
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
@@ -228,7 +246,7 @@ void attn_fwd_fp8(const AttnArgs a) {
           if (g >= 0) {
             u = ld16(qrow + ks * 64 + c4 * 8);
             if constexpr (kRope)
-              u = rope8(u, a.qrope + (static_cast<size_t>(g) * (D / 2) + ks * 32 + half * 16 +
+              u = rope8(u, a.qrope + (static_cast<size_t>(g) * (D / 2) + ks * 32 + qhalf * 16 +
                                       c4 * 4) * 2);
           }
           const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
@@ -428,8 +446,10 @@ void attn_fwd_fp8(const AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[db][i] *= vs_cur;
     const float l_tot = lacc[0];
-    finish_piece<D, kLse>(a, oacc, m_ref, l_tot, r, h, qbase, first_piece, w, wave, lane,
-                          s_ticket, sp);
+    unsigned epoch = a.epoch;
+    asm volatile("" : "+s"(epoch));
+    finish_piece<D, kLse>(a, oacc, m_ref, l_tot, r, h, qbase, first_piece, w, wave, lane_now(),
+                          s_ticket, sp, epoch);
   };
 
   // The pieces of this workgroup's range (one per row it touches).
