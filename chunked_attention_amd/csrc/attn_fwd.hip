@@ -20,8 +20,8 @@
 // the split and the merge of split rows live in attn_common.hpp.
 //
 // Instances (template flags): kLse (log-sum-exp output), kRope (q rotated at
-// its load), kRowsFirst (the plain call over ranges of more than two rows
-// walks a workgroup's pieces whole rows first; otherwise last first) and
+// its load), kRowsFirst (plain and RoPE calls over ranges of more than two
+// rows walk a workgroup's pieces whole rows first; otherwise last first) and
 // kActive (active-row calls: the split is taken in the kernel from the
 // device-side row count, with ranges kept inside one row where that costs
 // few steps).  Each is its own instance so that the others' code stays as
@@ -445,7 +445,8 @@ kvc_status launch_bf16(const AttnDesc& d, hipStream_t stream) {
   if (st != KVC_OK) return st;
   const dim3 grid(a.nwg), block(kThreads);
   // active-row calls have instances of their own (their split is taken in
-  // the kernel); whole rows first only on the plain call over long rows
+  // the kernel); whole rows first on the plain and RoPE calls whose ranges
+  // span more than two rows
   if (a.qcount) {
     if (a.qrope) {
       if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, true, false, true>), grid, block, 0, stream, a);
@@ -455,8 +456,13 @@ kvc_status launch_bf16(const AttnDesc& d, hipStream_t stream) {
       else hipLaunchKernelGGL((attn_fwd_bf16<D, false, false, false, true>), grid, block, 0, stream, a);
     }
   } else if (a.qrope) {
-    if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, true, false, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16<D, false, true, false, false>), grid, block, 0, stream, a);
+    if (rows_first(a.total, a.nwg, a.ntiles)) {
+      if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, true, true, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16<D, false, true, true, false>), grid, block, 0, stream, a);
+    } else {
+      if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, true, false, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_fwd_bf16<D, false, true, false, false>), grid, block, 0, stream, a);
+    }
   } else if (rows_first(a.total, a.nwg, a.ntiles)) {
     if (a.lse) hipLaunchKernelGGL((attn_fwd_bf16<D, true, false, true, false>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_fwd_bf16<D, false, false, true, false>), grid, block, 0, stream, a);

@@ -488,11 +488,16 @@ kvc_status launch_fp8_d(const AttnDesc& d, hipStream_t stream) {
   const kvc_status st = fill_args(d, kBk, a, stream);
   if (st != KVC_OK) return st;
   const dim3 grid(a.nwg), block(kThreads);
-  // whole rows first only on the plain call over long rows (RoPE and
-  // active-row calls keep one instance each)
+  // whole rows first on the plain and RoPE calls whose ranges span more
+  // than two rows (active-row calls share the last-first instances)
   if (a.qrope) {
-    if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_fp8<D, false, true, false>), grid, block, 0, stream, a);
+    if (!a.qcount && rows_first(a.total, a.nwg, a.ntiles)) {
+      if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_fwd_fp8<D, false, true, true>), grid, block, 0, stream, a);
+    } else {
+      if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, true, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((attn_fwd_fp8<D, false, true, false>), grid, block, 0, stream, a);
+    }
   } else if (!a.qcount && rows_first(a.total, a.nwg, a.ntiles)) {
     if (a.lse) hipLaunchKernelGGL((attn_fwd_fp8<D, true, false, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((attn_fwd_fp8<D, false, false, true>), grid, block, 0, stream, a);

@@ -115,6 +115,44 @@ def test_fused_rope_equals_prerotated_inputs(dtype, groups):
         plain.evict()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8_e4m3"])
+def test_fused_rope_three_frame_chunk_whole_rows_first(dtype):
+    # 4860-query chunks over 40 heads: 1520 query rows on 512 workgroups, so
+    # every range spans three or more rows and the RoPE call walks its
+    # pieces whole rows first, like the plain call on pre-rotated inputs.
+    # The two must agree bit for bit (chunk 0, then chunk 1 after a COMMIT).
+    w = synth.WORKLOADS["edit3"]
+    H, d, n, m, W = w.heads, w.head_dim, w.chunk_tokens, w.cond_tokens, w.window
+    st = synth.Stream(w, "baseline")
+    fused = ring(H, d, n, m, W, dtype)
+    plain = ring(H, d, n, m, W, dtype)
+    ck, cv = st.kv_cond()
+    tc = synth.rope_table(49, 100, m, d)
+    fused.cond(ck.cuda(), cv.cuda(), rope=tc.cuda())
+    plain.cond(O5.rotate_stored(ck, tc.numpy()).cuda(), cv.cuda())
+    for t in range(2):
+        k, v = st.kv_noisy(t)
+        q = st.q(t)
+        tk = synth.rope_table(49, t, n, d)
+        tq = synth.rope_table(49, 1000 + t, n, d)
+        fused.stage(k.cuda(), v.cuda(), rope=tk.cuda())
+        plain.stage(O5.rotate_stored(k, tk.numpy()).cuda(), v.cuda())
+        lf = torch.empty(H, n, device="cuda")
+        lp = torch.empty(H, n, device="cuda")
+        of = fused.attention(q.cuda(), lse=lf, rope=tq.cuda())
+        op = plain.attention(O5.rotate_stored(q, tq.numpy()).cuda(), lse=lp)
+        assert torch.equal(of.view(torch.int16), op.view(torch.int16)), f"t={t}"
+        assert torch.equal(lf, lp), f"t={t}"
+        of2 = fused.attention(q.cuda(), rope=tq.cuda())
+        op2 = plain.attention(O5.rotate_stored(q, tq.numpy()).cuda())
+        assert torch.equal(of2.view(torch.int16), op2.view(torch.int16)), f"t={t} no lse"
+        kc, vc = st.kv_clean(t)
+        fused.commit(kc.cuda(), vc.cuda(), rope=tk.cuda())
+        plain.commit(O5.rotate_stored(kc, tk.numpy()).cuda(), vc.cuda())
+        fused.evict()
+        plain.evict()
+
+
 @pytest.mark.parametrize("dist", ["baseline", "sharp", "peaky"])
 def test_rope_stream_parity(dist):
     # bf16 ring with reference and source groups, rotated keys and queries,
