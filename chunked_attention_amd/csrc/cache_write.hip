@@ -22,7 +22,9 @@
 // rotated keys, their scale taken over the rotated values.
 //
 // HBM-bound: each element is read once and written once.  One workgroup
-// handles 64 rows of one head; V goes through LDS for the transpose.
+// handles 64 rows of one head (bf16 keys with a rotation table: 64/G rows of
+// G heads, so that each table row is read once for G heads); V goes through
+// LDS for the transpose.
 #include "device_common.hpp"
 #include "kvc_internal.hpp"
 
@@ -45,11 +47,34 @@ __device__ __forceinline__ int pi64(int p) {
 
 // ---------------------------------------------------------------- bf16 ----
 
+// Transposed store of a block's V (64 keys of one head, staged in LDS rows of
+// D + 2 features): the block's keys are two 32-key tiles; row dd of tile b
+// gets its 32 keys (4 chunks of 8), in kappa order.
+template <int D>
+__device__ __forceinline__ void store_vt_bf16(const uint16_t* vtile, uint16_t* __restrict__ vtd,
+                                              int h, int pitch, int r0, int tid) {
+  constexpr int kLdsPitch = D + 2;
+  for (int c = tid; c < D * 8; c += kThreads) {
+    const int dd = c / 8;
+    const int ch = c % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = vtile[kappa(ch * 8 + 2 * j) * kLdsPitch + dd];
+      const uint32_t hi = vtile[kappa(ch * 8 + 2 * j + 1) * kLdsPitch + dd];
+      w[j] = lo | (hi << 16);
+    }
+    const int tile = (r0 >> 5) + (ch >> 2);
+    st16(vtd + static_cast<size_t>(h) * D * pitch + (static_cast<size_t>(tile) * D + dd) * 32 +
+             (ch & 3) * 8,
+         make_uint4(w[0], w[1], w[2], w[3]));
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void cache_write_bf16(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int rows, int pitch,
-    int heads, uint16_t* __restrict__ kd, uint16_t* __restrict__ vtd,
-    const float* __restrict__ rope) {
+    int heads, uint16_t* __restrict__ kd, uint16_t* __restrict__ vtd) {
   constexpr int kChunks = D / 8;         // 16-byte chunks per row
   constexpr int kLdsPitch = D + 2;       // u16 per LDS row; odd word count avoids conflicts
   __shared__ uint32_t vtile32[kRowsPerBlock * kLdsPitch / 2];
@@ -68,7 +93,6 @@ __global__ __launch_bounds__(kThreads) void cache_write_bf16(
       const size_t src = (static_cast<size_t>(r) * heads + h) * D + ch * 8;
       kv = ld16(k + src);
       vv = ld16(v + src);
-      if (rope) kv = rope8(kv, rope + (static_cast<size_t>(r) * (D / 2) + ch * 4) * 2);
     }
     st16(kd + (static_cast<size_t>(h) * pitch + r) * D + ch * 8, kv);
     uint32_t* dst = reinterpret_cast<uint32_t*>(vtile + row * kLdsPitch + ch * 8);
@@ -78,23 +102,64 @@ __global__ __launch_bounds__(kThreads) void cache_write_bf16(
     dst[3] = vv.w;
   }
   __syncthreads();
-  // transposed store: the block's 64 keys are two 32-key tiles; row dd of
-  // tile b gets its 32 keys (4 chunks of 8)
-  for (int c = tid; c < D * 8; c += kThreads) {
-    const int dd = c / 8;
-    const int ch = c % 8;
-    uint32_t w[4];
+  store_vt_bf16<D>(vtile, vtd, h, pitch, r0, tid);
+}
+
+// The same write for keys with a rotation table.  The table row of a token
+// is the same for every head, so within each group of G heads (G divides
+// H) the G workgroups over one block of 64 rows split the keys by rows, not
+// by heads: workgroup (block, h) rotates rows g*64/G .. (g+1)*64/G - 1 of
+// the block (g = h mod G) for all G heads of its group, reading each table
+// row once for G heads.  V is handled per head as above.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void cache_write_bf16_rope(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int rows, int pitch,
+    int heads, uint16_t* __restrict__ kd, uint16_t* __restrict__ vtd,
+    const float* __restrict__ rope) {
+  constexpr int kChunks = D / 8;
+  constexpr int kLdsPitch = D + 2;
+  constexpr int kRowsK = kRowsPerBlock / G;
+  static_assert(kRowsPerBlock % G == 0, "row share per head group");
+  __shared__ uint32_t vtile32[kRowsPerBlock * kLdsPitch / 2];
+  uint16_t* vtile = reinterpret_cast<uint16_t*>(vtile32);
+
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.x * kRowsPerBlock;
+  const int tid = threadIdx.x;
+  const int h0 = h - h % G;
+  const int rk0 = r0 + (h % G) * kRowsK;
+
+  for (int c = tid; c < kRowsK * kChunks; c += kThreads) {
+    const int r = rk0 + c / kChunks;
+    const int ch = c % kChunks;
+    uint4 kv[G];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = vtile[kappa(ch * 8 + 2 * j) * kLdsPitch + dd];
-      const uint32_t hi = vtile[kappa(ch * 8 + 2 * j + 1) * kLdsPitch + dd];
-      w[j] = lo | (hi << 16);
+    for (int j = 0; j < G; ++j) kv[j] = make_uint4(0, 0, 0, 0);
+    if (r < rows) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) kv[j] = ld16(k + (static_cast<size_t>(r) * heads + h0 + j) * D + ch * 8);
+      const RopeRow cs = rope_row(rope + (static_cast<size_t>(r) * (D / 2) + ch * 4) * 2);
+#pragma unroll
+      for (int j = 0; j < G; ++j) kv[j] = rope8(kv[j], cs);
     }
-    const int tile = (r0 >> 5) + (ch >> 2);
-    st16(vtd + static_cast<size_t>(h) * D * pitch + (static_cast<size_t>(tile) * D + dd) * 32 +
-             (ch & 3) * 8,
-         make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      st16(kd + (static_cast<size_t>(h0 + j) * pitch + r) * D + ch * 8, kv[j]);
   }
+  for (int c = tid; c < kRowsPerBlock * kChunks; c += kThreads) {
+    const int row = c / kChunks;
+    const int ch = c % kChunks;
+    const int r = r0 + row;
+    uint4 vv = make_uint4(0, 0, 0, 0);
+    if (r < rows) vv = ld16(v + (static_cast<size_t>(r) * heads + h) * D + ch * 8);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(vtile + row * kLdsPitch + ch * 8);
+    dst[0] = vv.x;
+    dst[1] = vv.y;
+    dst[2] = vv.z;
+    dst[3] = vv.w;
+  }
+  __syncthreads();
+  store_vt_bf16<D>(vtile, vtd, h, pitch, r0, tid);
 }
 
 // ----------------------------------------------------------------- fp8 ----
@@ -283,10 +348,22 @@ kvc_status launch_write(const CacheWriteDesc& d, hipStream_t s) {
   const dim3 block(kThreads);
   const dim3 grid(d.pitch / kRowsPerBlock, d.heads);
   if (d.kv_dtype == KVC_KV_BF16) {
-    hipLaunchKernelGGL(cache_write_bf16<D>, grid, block, 0, s,
-                       static_cast<const uint16_t*>(d.k), static_cast<const uint16_t*>(d.v),
-                       d.rows, d.pitch, d.heads, static_cast<uint16_t*>(d.k_dst),
-                       static_cast<uint16_t*>(d.vt_dst), d.rope);
+    const uint16_t* k = static_cast<const uint16_t*>(d.k);
+    const uint16_t* v = static_cast<const uint16_t*>(d.v);
+    uint16_t* kd = static_cast<uint16_t*>(d.k_dst);
+    uint16_t* vtd = static_cast<uint16_t*>(d.vt_dst);
+    if (!d.rope)
+      hipLaunchKernelGGL(cache_write_bf16<D>, grid, block, 0, s, k, v, d.rows, d.pitch, d.heads,
+                         kd, vtd);
+    else if (d.heads % 4 == 0)
+      hipLaunchKernelGGL((cache_write_bf16_rope<D, 4>), grid, block, 0, s, k, v, d.rows, d.pitch,
+                         d.heads, kd, vtd, d.rope);
+    else if (d.heads % 2 == 0)
+      hipLaunchKernelGGL((cache_write_bf16_rope<D, 2>), grid, block, 0, s, k, v, d.rows, d.pitch,
+                         d.heads, kd, vtd, d.rope);
+    else
+      hipLaunchKernelGGL((cache_write_bf16_rope<D, 1>), grid, block, 0, s, k, v, d.rows, d.pitch,
+                         d.heads, kd, vtd, d.rope);
   } else {
     const int nblk = (d.rows + kRowsPerBlock - 1) / kRowsPerBlock;
     hipLaunchKernelGGL(cache_amax_fp8<D>, dim3(nblk, d.heads), block, 0, s,

@@ -39,15 +39,21 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t b) {
 }
 
 // Rotary encoding of one 16-byte chunk of bf16 features (pairs p .. p+3 of a
-// token) by the angles of a float32 table row: t = (cos, sin) of the four
+// token) by the angles of a float32 table row: cs = (cos, sin) of the four
 // pairs.  x' = x cos - y sin, y' = x sin + y cos, each product and the
 // sum/difference rounded to float32 on its own (no fused multiply-add), then
 // rounded to bf16 (nearest, ties to even).
-__device__ __forceinline__ uint4 rope8(uint4 x, const float* __restrict__ t) {
-#pragma clang fp contract(off)
+struct RopeRow {
+  float cs[8];
+};
+__device__ __forceinline__ RopeRow rope_row(const float* __restrict__ t) {
   const float4 t0 = *reinterpret_cast<const float4*>(t);
   const float4 t1 = *reinterpret_cast<const float4*>(t + 4);
-  const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+  return RopeRow{{t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w}};
+}
+__device__ __forceinline__ uint4 rope8(uint4 x, const RopeRow& row) {
+#pragma clang fp contract(off)
+  const float* cs = row.cs;
   uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -64,6 +70,10 @@ __device__ __forceinline__ uint4 rope8(uint4 x, const float* __restrict__ t) {
     w[p] = lo | (hi << 16);
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
+}
+// the same with the table row read from t
+__device__ __forceinline__ uint4 rope8(uint4 x, const float* __restrict__ t) {
+  return rope8(x, rope_row(t));
 }
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
