@@ -290,38 +290,46 @@ __global__ __launch_bounds__(kThreads) void cache_quant_fp8(
   // (uniform per head), else the correctly rounded division
   const bool fast = fast_scale(sk) && fast_scale(sv);
   const float rk = __fdiv_rn(1.0f, sk), rv = __fdiv_rn(1.0f, sv);
-  auto qk = [&](float x) { return fast ? div_by_scale(x, sk, rk) : __fdiv_rn(x, sk); };
-  auto qv = [&](float x) { return fast ? div_by_scale(x, sv, rv) : __fdiv_rn(x, sv); };
-
-  for (int c = tid; c < kRowsPerBlock * kChunks; c += kThreads) {
-    const int row = c / kChunks;
-    const int ch = c % kChunks;
-    const int r = r0 + row;
-    uint32_t kc[2] = {0u, 0u}, vc[2] = {0u, 0u};
-    if (r < rows) {
-      const size_t src = (static_cast<size_t>(r) * heads + h) * D + ch * 8;
-      uint4 kv = ld16(k + src);
-      const uint4 vv = ld16(v + src);
-      if (rope) kv = rope8(kv, rope + (static_cast<size_t>(r) * (D / 2) + ch * 4) * 2);
-      const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-      const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+  // the rows, encoded with one of the two divisions (chosen once, so that
+  // the loop body is one straight block)
+  auto encode = [&](auto fast_tag) {
+    constexpr bool kFast = decltype(fast_tag)::value;
+    auto qk = [&](float x) { return kFast ? div_by_scale(x, sk, rk) : __fdiv_rn(x, sk); };
+    auto qv = [&](float x) { return kFast ? div_by_scale(x, sv, rv) : __fdiv_rn(x, sv); };
+    for (int c = tid; c < kRowsPerBlock * kChunks; c += kThreads) {
+      const int row = c / kChunks;
+      const int ch = c % kChunks;
+      const int r = r0 + row;
+      uint32_t kc[2] = {0u, 0u}, vc[2] = {0u, 0u};
+      if (r < rows) {
+        const size_t src = (static_cast<size_t>(r) * heads + h) * D + ch * 8;
+        uint4 kv = ld16(k + src);
+        const uint4 vv = ld16(v + src);
+        if (rope) kv = rope8(kv, rope + (static_cast<size_t>(r) * (D / 2) + ch * 4) * 2);
+        const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
+        const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t k01 = e4m3x2(qk(bf16_bits_to_float(kw[j] & 0xFFFFu)),
-                                    qk(bf16_bits_to_float(kw[j] >> 16)));
-        const uint32_t v01 = e4m3x2(qv(bf16_bits_to_float(vw[j] & 0xFFFFu)),
-                                    qv(bf16_bits_to_float(vw[j] >> 16)));
-        kc[j >> 1] |= k01 << (16 * (j & 1));
-        vc[j >> 1] |= v01 << (16 * (j & 1));
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t k01 = e4m3x2(qk(bf16_bits_to_float(kw[j] & 0xFFFFu)),
+                                      qk(bf16_bits_to_float(kw[j] >> 16)));
+          const uint32_t v01 = e4m3x2(qv(bf16_bits_to_float(vw[j] & 0xFFFFu)),
+                                      qv(bf16_bits_to_float(vw[j] >> 16)));
+          kc[j >> 1] |= k01 << (16 * (j & 1));
+          vc[j >> 1] |= v01 << (16 * (j & 1));
+        }
       }
+      *reinterpret_cast<uint2*>(kd + (static_cast<size_t>(h) * pitch + r) * D + ch * 8) =
+          make_uint2(kc[0], kc[1]);
+      // LDS rows are 4-byte aligned only: two 32-bit stores
+      uint32_t* vdst = reinterpret_cast<uint32_t*>(vtile + row * kLdsPitch + ch * 8);
+      vdst[0] = vc[0];
+      vdst[1] = vc[1];
     }
-    *reinterpret_cast<uint2*>(kd + (static_cast<size_t>(h) * pitch + r) * D + ch * 8) =
-        make_uint2(kc[0], kc[1]);
-    // LDS rows are 4-byte aligned only: two 32-bit stores
-    uint32_t* vdst = reinterpret_cast<uint32_t*>(vtile + row * kLdsPitch + ch * 8);
-    vdst[0] = vc[0];
-    vdst[1] = vc[1];
-  }
+  };
+  if (fast)
+    encode(std::true_type{});
+  else
+    encode(std::false_type{});
   __syncthreads();
   // transposed store: the block is one 64-key tile; row dd gets its 64
   // keys (4 chunks of 16)
