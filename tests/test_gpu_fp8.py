@@ -8,6 +8,7 @@
   boundary; the kernel's own fp8 rounding of Q and P is part of the error.
 """
 import dataclasses
+import math
 
 import numpy as np
 import pytest
@@ -139,6 +140,21 @@ def test_fp8_config_stream_sampled(dist):
         (o, ref, st), = run.chunk(t, lse=True)
         check_fp8(st, f"fp8 cfg {dist} t={t}")
         print(f"fp8 cfg {dist} t={t}: max-abs {st['max_abs']:.2e} rel-L2 {st['rel_l2']:.2e}")
+
+
+def test_fp8_head_dim_64_at_720p_size():
+    # the fp8 configuration with 64-wide heads (40 heads, 1620 queries, W = 3):
+    # 520 query rows on 512 workgroups, split and merged; oracle on the
+    # dequantised K/V of 3 heads at chunks 3 and 4
+    w = dataclasses.replace(synth.WORKLOADS["fp8"], name="fp8-d64", head_dim=64,
+                            std=1.0 / math.sqrt(64), seed=14)
+    heads = [0, 17, 39]
+    run = StreamRun(synth.Stream(w, "baseline"), fp8_ring(w), fp8=True, heads=heads)
+    for t in range(5):
+        (o, ref, st), = run.chunk(t, lse=True, check=t >= 3)
+        if t >= 3:
+            check_fp8(st, f"fp8 d=64 t={t}")
+            print(f"fp8 d=64 t={t}: max-abs {st['max_abs']:.2e} rel-L2 {st['rel_l2']:.2e}")
 
 
 def test_fp8_config_whole_stream_sampled_chunks():

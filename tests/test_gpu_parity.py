@@ -100,6 +100,23 @@ def test_720p_stream_parity_sampled_heads(dist):
     assert run.ring.info().n_window == 3
 
 
+@pytest.mark.parametrize("dist", ["baseline", "peaky"])
+def test_head_dim_64_at_720p_size(dist):
+    # the 720p chunk shape with 64-wide heads (40 heads, 1620 queries, 256
+    # condition tokens, W = 3): 520 query rows on 512 workgroups, so nearly
+    # every row is split and merged, as in the 128-wide call.  Oracle on 3
+    # heads at chunks 3 and 4 (8356 keys from chunk 4).
+    w = dataclasses.replace(synth.WORKLOADS["720p"], name="720p-d64", head_dim=64,
+                            std=1.0 / math.sqrt(64), seed=13)
+    heads = [0, 17, 39]
+    run = StreamRun(synth.Stream(w, dist), ring_for(w), heads=heads)
+    for t in range(5):
+        (o, ref, st), = run.chunk(t, lse=True, check=t >= 3)
+        if t >= 3:
+            assert_bf16_parity(st, f"720p d=64 {dist} t={t}")
+            assert st["lse_max_abs"] < LSE_BF16_BOUND, st
+
+
 def test_720p_steady_chunk_all_heads():
     # one steady-state chunk (t = 4, 8356 keys) checked on every head
     w = synth.WORKLOADS["720p"]
